@@ -1,0 +1,127 @@
+"""CPU oracle for image resize (linear and nearest-neighbour).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never calls it and shares no code
+with it.
+
+The arithmetic lives in ``resize_oracle.c`` (plain C, built with gcc into
+``liboracle_resize.so``); this module only marshals numpy arrays into it.
+What the C file computes, and which passage of the pages each step follows,
+is stated in its header:
+
+* "From Prototype to Performance: Optimizing OpenCV Resize on Volcanic GPUs"
+  (Imagination blog), sections "Step 1: Build a reliable reference path" and
+  "Naive resize with linear sampling": each output pixel centre is mapped back
+  into the input and sampled with a linear filter.
+* hnwysp.cn news/129086 (CUDA nearest and bilinear interpolation), s2.1
+  nearest formula, s2.2 bilinear formula, s3.3 last-pixel limit on the second
+  neighbour, s6.1 clamping, s6.2 fixed point.
+
+Pins (checked in ``tests/test_oracle_pins.py``): identity at scale 1,
+constant images, exact 2:1 downscale = 2x2 average, linear ramps, nearest
+closed form for integer upscales, exact-rational bilinear within the
+quantisation bound, and torch's float64 ``interpolate`` as a library special
+case.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "resize_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_resize.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, no intrinsics, no vectorisation hints)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        vp = ctypes.c_void_p
+        for name in ("oracle_linear_u8", "oracle_linear_f32"):
+            f = getattr(lib, name)
+            f.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, i64, i64]
+            f.restype = ci
+        lib.oracle_nearest.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, i64, i64]
+        lib.oracle_nearest.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _as_nhwc(src: np.ndarray) -> np.ndarray:
+    if src.ndim == 2:
+        src = src[None, :, :, None]
+    elif src.ndim == 3:
+        src = src[None]
+    if src.ndim != 4:
+        raise ValueError("expected HW, HWC or NHWC array, got shape %r" % (src.shape,))
+    return np.ascontiguousarray(src)
+
+
+def _rows(N, dH, rows):
+    if rows is None:
+        return 0, N * dH
+    r0, r1 = rows
+    if not (0 <= r0 <= r1 <= N * dH):
+        raise ValueError("row range out of bounds")
+    return r0, r1
+
+
+def resize_linear(src: np.ndarray, dH: int, dW: int, rows=None) -> np.ndarray:
+    """Linear (bilinear) resize of an NHWC uint8 or float32 array to dH x dW.
+
+    ``rows=(r0, r1)`` computes only global output rows r0..r1-1 (row index
+    n * dH + dy) and returns them as an array of shape (r1 - r0, dW, C);
+    without it the whole N x dH x dW x C result is returned.
+    """
+    src = _as_nhwc(src)
+    N, H, W, C = src.shape
+    r0, r1 = _rows(N, dH, rows)
+    lib = _load()
+    if src.dtype == np.uint8:
+        fn = lib.oracle_linear_u8
+    elif src.dtype == np.float32:
+        fn = lib.oracle_linear_f32
+    else:
+        raise TypeError("oracle supports uint8 and float32, got %s" % src.dtype)
+    full = np.empty((N * dH, dW, C), dtype=src.dtype)
+    rc = fn(src.ctypes.data, full.ctypes.data, N, H, W, C, dH, dW, r0, r1)
+    if rc != 0:
+        raise ValueError("oracle rejected arguments (code %d)" % rc)
+    if rows is not None:
+        return full[r0:r1].copy()
+    return full.reshape(N, dH, dW, C)
+
+
+def resize_nearest(src: np.ndarray, dH: int, dW: int, rows=None) -> np.ndarray:
+    """Nearest-neighbour resize of an NHWC array (any element type) to dH x dW."""
+    src = _as_nhwc(src)
+    N, H, W, C = src.shape
+    r0, r1 = _rows(N, dH, rows)
+    full = np.empty((N * dH, dW, C), dtype=src.dtype)
+    rc = _load().oracle_nearest(src.ctypes.data, full.ctypes.data, src.itemsize,
+                                N, H, W, C, dH, dW, r0, r1)
+    if rc != 0:
+        raise ValueError("oracle rejected arguments (code %d)" % rc)
+    if rows is not None:
+        return full[r0:r1].copy()
+    return full.reshape(N, dH, dW, C)

@@ -1,0 +1,361 @@
+"""Pins for the CPU oracle: facts the pages and the mathematics fix.
+
+None of these re-types the oracle's arithmetic.  Each checks the oracle
+against something independent of it: a closed form, an invariant, exact
+rational arithmetic in a different (separable) form, or torch's float64
+``interpolate``, which is the textbook half-pixel bilinear / nearest-exact
+resize and serves as a library special case.
+
+Sources: "From Prototype to Performance: Optimizing OpenCV Resize on Volcanic
+GPUs" ("Naive resize with linear sampling": centre + 0.5 scaled into the
+input, linear filter), and hnwysp.cn news/129086 (s2.1 nearest, s2.2
+bilinear formula, s6.1 clamping, s6.2 fixed point).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bilinear_image_resize_amd.workloads import WORKLOADS, make_source
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def rand_img(r, shape, dtype):
+    if dtype == np.uint8:
+        return r.integers(0, 256, size=shape, dtype=np.uint8)
+    return r.random(size=shape, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------
+# identity: scale 1 maps every pixel centre onto itself
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [np.uint8, np.float32])
+def test_identity(dtype):
+    r = rng(1)
+    for _ in range(40):
+        N, H, W = r.integers(1, 3), r.integers(1, 40), r.integers(1, 40)
+        C = int(r.choice([1, 3, 4]))
+        s = rand_img(r, (N, H, W, C), dtype)
+        assert np.array_equal(oracle.resize_linear(s, H, W), s)
+        assert np.array_equal(oracle.resize_nearest(s, H, W), s)
+
+
+# --------------------------------------------------------------------------
+# constant images stay constant (weights sum to one, any scale, any border)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [np.uint8, np.float32])
+def test_constant(dtype):
+    r = rng(2)
+    for _ in range(60):
+        H, W = r.integers(1, 30, size=2)
+        dH, dW = r.integers(1, 70, size=2)
+        C = int(r.choice([1, 3, 4]))
+        vals = rand_img(r, (C,), dtype)
+        s = np.broadcast_to(vals, (1, H, W, C)).copy()
+        out = oracle.resize_linear(s, dH, dW)
+        assert np.array_equal(out, np.broadcast_to(vals, out.shape))
+
+
+# --------------------------------------------------------------------------
+# an exact 2:1 downscale is the 2x2 block average (half-pixel centres put the
+# sample exactly between four pixels).  A corner-aligned map would return the
+# top-left pixel of each block instead, and truncation instead of
+# round-half-up would turn {0,0,0,2} into 0 instead of 1.
+# --------------------------------------------------------------------------
+def test_half_down_u8_block_average():
+    r = rng(3)
+    for _ in range(30):
+        N, h, w = r.integers(1, 3), r.integers(1, 20), r.integers(1, 20)
+        C = int(r.choice([1, 3, 4]))
+        s = rand_img(r, (N, 2 * h, 2 * w, C), np.uint8)
+        blocks = s.reshape(N, h, 2, w, 2, C).astype(np.int64).sum(axis=(2, 4))
+        expect = ((blocks + 2) // 4).astype(np.uint8)
+        assert np.array_equal(oracle.resize_linear(s, h, w), expect)
+    tie = np.array([[0, 0], [0, 2]], dtype=np.uint8)
+    assert oracle.resize_linear(tie, 1, 1).item() == 1
+    tie = np.array([[0, 0], [0, 1]], dtype=np.uint8)   # 0.25 rounds down
+    assert oracle.resize_linear(tie, 1, 1).item() == 0
+
+
+def test_half_down_f32_block_mean():
+    r = rng(4)
+    for _ in range(30):
+        N, h, w = r.integers(1, 3), r.integers(1, 20), r.integers(1, 20)
+        C = int(r.choice([1, 3, 4]))
+        s = rand_img(r, (N, 2 * h, 2 * w, C), np.float32)
+        mean = s.reshape(N, h, 2, w, 2, C).astype(np.float64).mean(axis=(2, 4))
+        out = oracle.resize_linear(s, h, w)
+        assert np.max(np.abs(out - mean)) <= 6e-8
+
+
+def test_full_4k_frame_is_block_average():
+    """The 4K RGB frame -> 1080p at its real size: every output is a 2x2 mean."""
+    w = WORKLOADS["4k"]
+    s = make_source(w)
+    blocks = s.reshape(1, w.dH, 2, w.dW, 2, 3).astype(np.int32).sum(axis=(2, 4))
+    expect = ((blocks + 2) // 4).astype(np.uint8)
+    assert np.array_equal(oracle.resize_linear(s, w.dH, w.dW), expect)
+
+
+# --------------------------------------------------------------------------
+# linear ramps are reproduced: bilinear interpolation of p = a + bx*x + by*y
+# sampled at the clamped source coordinate gives the ramp there.
+# --------------------------------------------------------------------------
+def src_coord(d, n_in, n_out):
+    """Half-pixel source coordinate, clamped to [0, n_in - 1], as a Fraction."""
+    x = (Fraction(d) + Fraction(1, 2)) * Fraction(n_in, n_out) - Fraction(1, 2)
+    return min(max(x, Fraction(0)), Fraction(n_in - 1))
+
+
+def test_ramp_f32_any_scale():
+    r = rng(5)
+    for _ in range(40):
+        H, W = r.integers(1, 24, size=2)
+        dH, dW = r.integers(1, 50, size=2)
+        a, bx, by = (int(v) / 64.0 for v in r.integers(-64, 64, size=3))
+        ys, xs = np.mgrid[0:H, 0:W]
+        s = (a + bx * xs + by * ys).astype(np.float32)[None, :, :, None]
+        out = oracle.resize_linear(s, dH, dW)[0, :, :, 0]
+        for dy in range(dH):
+            sy = float(src_coord(dy, H, dH))
+            for dx in range(dW):
+                sx = float(src_coord(dx, W, dW))
+                assert abs(out[dy, dx] - (a + bx * sx + by * sy)) <= 2e-6
+
+
+@pytest.mark.parametrize("shape", [((6, 5), (12, 10)), ((5, 7), (20, 28)),
+                                   ((16, 12), (8, 6)), ((12, 16), (3, 4)),
+                                   ((3, 9), (24, 18))])
+def test_ramp_u8_dyadic_scales(shape):
+    """At scales whose weights are exact 11-bit fractions the u8 result is the
+    ramp at the source coordinate, rounded half up."""
+    (H, W), (dH, dW) = shape
+    checked = 0
+    for a, bx, by in ((3, 7, 11), (200, -9, -4), (0, 20, 1), (0, 3, 5), (255, -4, -7)):
+        ys, xs = np.mgrid[0:H, 0:W]
+        vals = a + bx * xs + by * ys
+        if vals.min() < 0 or vals.max() > 255:
+            continue
+        checked += 1
+        s = vals.astype(np.uint8)[None, :, :, None]
+        out = oracle.resize_linear(s, dH, dW)[0, :, :, 0]
+        for dy in range(dH):
+            sy = src_coord(dy, H, dH)
+            for dx in range(dW):
+                sx = src_coord(dx, W, dW)
+                v = a + bx * sx + by * sy
+                assert out[dy, dx] == int(np.floor(v + Fraction(1, 2)))
+    assert checked >= 2
+
+
+# --------------------------------------------------------------------------
+# exact rational bilinear (separable form: lerp along x on both rows, then
+# along y) - the u8 result is within the fixed-point bound of it:
+# two 11-bit weight roundings (255/4096 each) plus the final rounding 1/2.
+# --------------------------------------------------------------------------
+def exact_bilinear(img, dH, dW):
+    H, W = img.shape
+    out = np.empty((dH, dW), dtype=object)
+    for dy in range(dH):
+        y = src_coord(dy, H, dH)
+        j = int(np.floor(y)); v = y - j; j1 = min(j + 1, H - 1)
+        for dx in range(dW):
+            x = src_coord(dx, W, dW)
+            i = int(np.floor(x)); u = x - i; i1 = min(i + 1, W - 1)
+            top = int(img[j, i]) + u * (int(img[j, i1]) - int(img[j, i]))
+            bot = int(img[j1, i]) + u * (int(img[j1, i1]) - int(img[j1, i]))
+            out[dy, dx] = top + v * (bot - top)
+    return out
+
+
+def test_u8_within_fixed_point_bound_of_exact():
+    r = rng(6)
+    worst = Fraction(0)
+    for _ in range(150):
+        H, W = r.integers(1, 8, size=2)
+        dH, dW = r.integers(1, 10, size=2)
+        img = r.integers(0, 256, size=(H, W), dtype=np.uint8)
+        ex = exact_bilinear(img, dH, dW)
+        out = oracle.resize_linear(img, dH, dW)[0, :, :, 0]
+        for dy in range(dH):
+            for dx in range(dW):
+                d = abs(Fraction(int(out[dy, dx])) - ex[dy, dx])
+                worst = max(worst, d)
+    assert worst <= Fraction(1, 2) + Fraction(2 * 255, 4096)
+
+
+# --------------------------------------------------------------------------
+# library special case: torch float64 interpolate (half-pixel centres,
+# align_corners=False, no antialias) is the real-valued bilinear resize.
+# --------------------------------------------------------------------------
+def torch_bilinear(s, dH, dW):
+    t = torch.from_numpy(s.astype(np.float64)).permute(0, 3, 1, 2)
+    o = torch.nn.functional.interpolate(t, size=(dH, dW), mode="bilinear",
+                                        align_corners=False, antialias=False)
+    return o.permute(0, 2, 3, 1).numpy()
+
+
+def test_f32_matches_torch_float64():
+    r = rng(7)
+    for _ in range(200):
+        N = int(r.integers(1, 3)); C = int(r.choice([1, 3, 4]))
+        H, W = r.integers(1, 40, size=2)
+        dH, dW = r.integers(1, 60, size=2)
+        s = rand_img(r, (N, H, W, C), np.float32)
+        ref = torch_bilinear(s, dH, dW)
+        out = oracle.resize_linear(s, dH, dW)
+        # the oracle rounds a double result to float once: <= 1/2 ulp(1)
+        assert np.max(np.abs(out.astype(np.float64) - ref)) <= 6e-8
+
+
+def test_u8_matches_torch_at_dyadic_scales():
+    """Weights 0, 1/4, 1/2, 3/4 are exact in 11 bits: u8 = round-half-up of the
+    float64 value (which is exact for these weights)."""
+    r = rng(8)
+    for (H, W, dH, dW) in ((7, 9, 14, 18), (8, 12, 4, 6), (5, 6, 20, 24), (30, 17, 60, 34)):
+        s = rand_img(r, (2, H, W, 3), np.uint8)
+        ref = torch_bilinear(s, dH, dW)
+        assert np.array_equal(oracle.resize_linear(s, dH, dW),
+                              np.floor(ref + 0.5).astype(np.uint8))
+
+
+def test_u8_within_bound_of_torch_random_scales():
+    r = rng(9)
+    for _ in range(100):
+        H, W = r.integers(1, 40, size=2)
+        dH, dW = r.integers(1, 60, size=2)
+        s = rand_img(r, (1, H, W, 3), np.uint8)
+        ref = torch_bilinear(s, dH, dW)
+        out = oracle.resize_linear(s, dH, dW).astype(np.float64)
+        assert np.max(np.abs(out - ref)) <= 0.5 + 2 * 255 / 4096 + 1e-9
+
+
+def test_full_up2x_matches_torch():
+    """1080p grey -> 2160x3840 at its real size: weights 1/4, 3/4 are exact."""
+    w = WORKLOADS["up2x"]
+    s = make_source(w)
+    ref = torch_bilinear(s, w.dH, w.dW)
+    assert np.array_equal(oracle.resize_linear(s, w.dH, w.dW),
+                          np.floor(ref + 0.5).astype(np.uint8))
+
+
+# --------------------------------------------------------------------------
+# nearest: closed forms and torch's nearest-exact
+# --------------------------------------------------------------------------
+def test_nearest_integer_upscale_replicates():
+    r = rng(10)
+    for k in (2, 3, 4, 5):
+        s = rand_img(r, (2, 7, 5, 3), np.uint8)
+        out = oracle.resize_nearest(s, 7 * k, 5 * k)
+        assert np.array_equal(out, s.repeat(k, axis=1).repeat(k, axis=2))
+
+
+def test_nearest_integer_downscale_picks_centre():
+    """W = k*dW: the centre of output pixel d lands at k*d + (k-1)/2; rounding
+    half up picks k*d + k//2 (4 -> 2 picks columns 1 and 3)."""
+    r = rng(11)
+    for k in (2, 3, 4):
+        s = rand_img(r, (1, 4 * k, 6 * k, 1), np.float32)
+        out = oracle.resize_nearest(s, 4, 6)
+        assert np.array_equal(out, s[:, k // 2::k, k // 2::k])
+
+
+def test_full_up2x_nearest_replicates():
+    w = WORKLOADS["up2x"]
+    s = make_source(w)
+    out = oracle.resize_nearest(s, w.dH, w.dW)
+    assert np.array_equal(out, s.repeat(2, axis=1).repeat(2, axis=2))
+
+
+def test_nearest_matches_torch_nearest_exact():
+    """torch computes floor((d + 0.5) * in / out) in floating point; where the
+    exact value is an integer its rounding may land one pixel low, so those
+    rows and columns are left to the closed-form tests above."""
+    r = rng(12)
+    compared = 0
+    for _ in range(200):
+        H, W = (int(v) for v in r.integers(1, 40, size=2))
+        dH, dW = (int(v) for v in r.integers(1, 60, size=2))
+        s = rand_img(r, (1, H, W, 2), np.float32)
+        t = torch.from_numpy(s.astype(np.float64)).permute(0, 3, 1, 2)
+        ref = torch.nn.functional.interpolate(t, size=(dH, dW), mode="nearest-exact")
+        ref = ref.permute(0, 2, 3, 1).numpy().astype(np.float32)
+        out = oracle.resize_nearest(s, dH, dW)
+        rows = [d for d in range(dH) if ((Fraction(d) + Fraction(1, 2)) * Fraction(H, dH)).denominator != 1]
+        cols = [d for d in range(dW) if ((Fraction(d) + Fraction(1, 2)) * Fraction(W, dW)).denominator != 1]
+        sub = np.ix_([0], rows, cols, [0, 1])
+        assert np.array_equal(out[sub], ref[sub])
+        compared += len(rows) * len(cols)
+    assert compared > 100000
+
+
+# --------------------------------------------------------------------------
+# layout invariants: transpose, horizontal flip, channels, batch
+# --------------------------------------------------------------------------
+def test_transpose_equivariance():
+    r = rng(13)
+    for dtype in (np.uint8, np.float32):
+        for _ in range(30):
+            H, W = r.integers(1, 30, size=2)
+            dH, dW = r.integers(1, 50, size=2)
+            s = rand_img(r, (1, H, W, 3), dtype)
+            a = oracle.resize_linear(s, dH, dW)
+            b = oracle.resize_linear(s.transpose(0, 2, 1, 3), dW, dH).transpose(0, 2, 1, 3)
+            if dtype == np.uint8:   # weight product is symmetric, exact integers
+                assert np.array_equal(a, b)
+            else:
+                assert np.max(np.abs(a - b)) <= 1.2e-7
+            na = oracle.resize_nearest(s, dH, dW)
+            nb = oracle.resize_nearest(s.transpose(0, 2, 1, 3), dW, dH).transpose(0, 2, 1, 3)
+            assert np.array_equal(na, nb)
+
+
+def test_flip_equivariance():
+    """Mirroring input and output together: the half-pixel map is symmetric.
+    f32 exactly up to rounding; u8 at scales whose weights are not 11-bit
+    half-way ties (a tie rounds up on one side and down on the other)."""
+    r = rng(14)
+    for _ in range(30):
+        H, W = r.integers(1, 30, size=2)
+        dH, dW = r.integers(1, 50, size=2)
+        s = rand_img(r, (1, H, W, 1), np.float32)
+        a = oracle.resize_linear(s, dH, dW)[:, :, ::-1]
+        b = oracle.resize_linear(s[:, :, ::-1], dH, dW)
+        assert np.max(np.abs(a - b)) <= 1.2e-7
+    for (H, W, dH, dW) in ((48, 64, 72, 96), (20, 30, 10, 15), (9, 11, 36, 44)):
+        s = rand_img(r, (1, H, W, 3), np.uint8)
+        a = oracle.resize_linear(s, dH, dW)[:, ::-1, ::-1]
+        b = oracle.resize_linear(s[:, ::-1, ::-1], dH, dW)
+        assert np.array_equal(a, b)
+
+
+def test_channel_and_batch_independence():
+    r = rng(15)
+    for dtype in (np.uint8, np.float32):
+        s = rand_img(r, (3, 13, 17, 4), dtype)
+        full = oracle.resize_linear(s, 29, 11)
+        for n in range(3):
+            for c in range(4):
+                one = oracle.resize_linear(s[n:n + 1, :, :, c:c + 1], 29, 11)
+                assert np.array_equal(one, full[n:n + 1, :, :, c:c + 1])
+
+
+def test_row_ranges_compose():
+    r = rng(16)
+    s = rand_img(r, (2, 11, 13, 3), np.uint8)
+    full = oracle.resize_linear(s, 7, 19).reshape(14, 19, 3)
+    parts = [oracle.resize_linear(s, 7, 19, rows=(a, b)) for a, b in ((0, 5), (5, 6), (6, 14))]
+    assert np.array_equal(np.concatenate(parts), full)
+
+
+def test_output_within_source_range():
+    r = rng(17)
+    for _ in range(30):
+        s = rand_img(r, (1, 9, 9, 1), np.uint8) // 2 + 40
+        out = oracle.resize_linear(s, int(r.integers(1, 30)), int(r.integers(1, 30)))
+        assert out.min() >= s.min() and out.max() <= s.max()
