@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Throughput of the linear resize on one MI355X.
+
+Default workload: one RGB uint8 frame 2160 x 3840 (HWC) resized linearly to
+1080 x 1920 - the 4K -> 1080p case.  A step is one resize_linear call over one
+frame.  Inputs are seeded synthetic frames (smooth gradients + noise) already
+resident in HBM; the step rotates over enough (src, dst) buffer pairs that
+their total exceeds twice the 256 MB Infinity Cache, so each step reads its
+source from HBM, not from cache.
+
+Prints ONE JSON line with: Gpix/s (dst pixels per second, whole job), the
+kernel's HBM roofline (algorithmic bytes = src read once + dst written once,
+over the kernel's average duration measured with HIP events on the launch
+stream), and the CPU oracle timed on the host cores as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload 4k] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
+
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
+# dispatch, summed over the 8 XCDs), each scaled by the factor a plain copy of
+# known size reads on the same counter.  None until taken for the current
+# kernel; profiles/ holds the runs these come from.
+MEASURED_TRAFFIC = {}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--workload", default="4k")
+    p.add_argument("--mode", default=None, help="linear (default) or nearest")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
+    return p.parse_args()
+
+
+def cpu_baseline(w, src_np, mode, budget_s):
+    """The CPU oracle as it stands, on the host cores, over whole frames of
+    the same workload, repeated until about budget_s seconds have passed."""
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows_total = w.batch * w.dH
+    fn = oracle.resize_linear if mode == "linear" else oracle.resize_nearest
+    fn(src_np[:1], 1, 1)  # load the library outside the clock
+
+    def one_frame():
+        bounds = [rows_total * k // threads for k in range(threads + 1)]
+        ts = [threading.Thread(target=fn, args=(src_np, w.dH, w.dW),
+                               kwargs={"rows": (bounds[k], bounds[k + 1])})
+              for k in range(threads) if bounds[k + 1] > bounds[k]]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_frame()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / reps
+    return {
+        "value": round(w.dst_pixels / per / 1e9, 4),
+        "unit": "Gpix/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d whole %s frame(s), %.1f s, %.2f ms per frame, output rows split "
+                  "over %d host threads" % (reps, w.name, el, per * 1e3, threads),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bilinear_image_resize_amd as R
+    from bilinear_image_resize_amd.workloads import WORKLOADS, make_source
+
+    w = WORKLOADS[args.workload]
+    mode = args.mode or w.modes[0]
+    if mode not in w.modes:
+        sys.exit("workload %s has no %s mode" % (w.name, mode))
+    dev = torch.device("cuda:0")
+    R._load()
+    fn = R.resize_linear if mode == "linear" else R.resize_nearest
+
+    src_np = make_source(w)
+    tdt = torch.uint8 if w.dtype == "u8" else torch.float32
+    pair_bytes = w.src_bytes + w.dst_bytes
+    pairs = 1 if args.warm else max(2, -(-2 * INFINITY_CACHE_BYTES // pair_bytes))
+    src0 = torch.from_numpy(src_np).to(dev)
+    srcs = [src0] + [src0.clone() for _ in range(pairs - 1)]
+    dsts = [torch.empty(w.dst_shape, dtype=tdt, device=dev) for _ in range(pairs)]
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize(dev)
+
+    for i in range(args.warmup):
+        fn(srcs[i % pairs], dsts[i % pairs], stream)
+    torch.cuda.synchronize(dev)
+
+    # timed region: K steps; an event pair brackets every launch on the launch
+    # stream, so the kernel's own duration is read from the same run.
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        fn(srcs[i % pairs], dsts[i % pairs], stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    ker_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    trim = K // 10 if K >= 10 else 0
+    kept = ker_ms[trim:K - trim] if trim else ker_ms
+    ker_avg_ms = sum(kept) / len(kept)
+
+    ms_per_step = wall * 1e3 / K
+    gpix = w.dst_pixels / (ms_per_step * 1e-3) / 1e9
+    alg_bytes = pair_bytes
+    achieved = alg_bytes / (ker_avg_ms * 1e-3) / 1e9
+
+    # correctness of what was timed: the last buffer written, vs the oracle
+    if not args.no_cpu:
+        import oracle
+        ref = (oracle.resize_linear if mode == "linear" else oracle.resize_nearest)(src_np, w.dH, w.dW)
+        got = dsts[(K - 1) % pairs].cpu().numpy()
+        ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
+        if not ok:
+            sys.exit("bench output disagrees with the oracle")
+
+    traffic = MEASURED_TRAFFIC.get((w.name, mode))
+    line = {
+        "metric": "bilinear resize Gpix/s + HBM GB/s (% of peak), RGB u8 4K->1080p, 1 GPU",
+        "value": round(gpix, 3),
+        "unit": "Gpix/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s" % (
+                w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode),
+            "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
+            "mode": mode, "cache": "warm (1 pair)" if args.warm else "cold (%d rotating pairs)" % pairs,
+        },
+        "hbm_GBps_wall": round(pair_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernel_us": round(ker_avg_ms * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, src_np, mode, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+// C ABI of libmi_resize.so: argument checks, kernel selection, launch.
+// The contract (layout, ownership, errors, limits) is in include/mi_resize.h.
+#include "mi_resize.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "resize_kernels.hpp"
+
+namespace {
+
+using namespace mirsz;
+
+constexpr int kMaxDim = 65535;
+constexpr long long kMaxOutPixels = 1LL << 40;
+// Workgroups a launch aims for: 8 per CU on 256 CUs keeps every SIMD busy
+// with several waves while each lane still amortises its column taps over a
+// band of rows.
+constexpr long long kTargetBlocks = 2048;
+// Cap for grid-stride kernels, keeping every launch far below the 2^32
+// work-items a grid dimension can hold.
+constexpr long long kMaxStrideBlocks = 65536;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool env_flag(const char *name)
+{
+    const char *v = getenv(name);
+    return v && v[0] && strcmp(v, "0") != 0;
+}
+
+int check_args(const void *src, const void *dst, int batch, int H, int W, int C, int dtype,
+               int dH, int dW)
+{
+    if (!src || !dst) return MI_RESIZE_ERR_NULL;
+    if (dtype != MI_RESIZE_U8 && dtype != MI_RESIZE_F32) return MI_RESIZE_ERR_DTYPE;
+    if (C != 1 && C != 3 && C != 4) return MI_RESIZE_ERR_CHANNELS;
+    if (batch < 1 || H < 1 || W < 1 || dH < 1 || dW < 1) return MI_RESIZE_ERR_SHAPE;
+    if (H > kMaxDim || W > kMaxDim || dH > kMaxDim || dW > kMaxDim) return MI_RESIZE_ERR_SHAPE;
+    if ((long long)batch * dH * dW > kMaxOutPixels) return MI_RESIZE_ERR_SHAPE;
+    const size_t es = dtype == MI_RESIZE_U8 ? 1 : 4;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    const uintptr_t s1 = s0 + (size_t)batch * H * W * C * es;
+    const uintptr_t d1 = d0 + (size_t)batch * dH * dW * C * es;
+    if (s0 < d1 && d0 < s1) return MI_RESIZE_ERR_OVERLAP;
+    return MI_RESIZE_OK;
+}
+
+struct Grid {
+    unsigned blocks;
+    int rows_per_block;
+    int col_blocks;
+};
+
+// Row-band grid shared by the generic kernels.
+Grid band_grid(long long rows_total, int dW)
+{
+    Grid g;
+    g.col_blocks = (dW + kBlock - 1) / kBlock;
+    long long per_row = g.col_blocks;
+    long long rpb = (rows_total * per_row + kTargetBlocks - 1) / kTargetBlocks;
+    if (rpb < 1) rpb = 1;
+    g.rows_per_block = (int)rpb;
+    g.blocks = (unsigned)(((rows_total + rpb - 1) / rpb) * per_row);
+    return g;
+}
+
+int launched()
+{
+    return hipGetLastError() == hipSuccess ? MI_RESIZE_OK : MI_RESIZE_ERR_HIP;
+}
+
+template <typename T, int C>
+int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                          hipStream_t st)
+{
+    const long long rows = (long long)batch * dH;
+    const Grid g = band_grid(rows, dW);
+    const bool pix4 = C == 4 && aligned(src, 4 * sizeof(T)) && aligned(dst, 4 * sizeof(T));
+    if (pix4) {
+        hipLaunchKernelGGL((linear_generic<T, C, C == 4>), dim3(g.blocks), dim3(kBlock), 0, st,
+                           (const T *)src, (T *)dst, H, W, dH, dW, rows, g.rows_per_block,
+                           g.col_blocks);
+    } else {
+        hipLaunchKernelGGL((linear_generic<T, C, false>), dim3(g.blocks), dim3(kBlock), 0, st,
+                           (const T *)src, (T *)dst, H, W, dH, dW, rows, g.rows_per_block,
+                           g.col_blocks);
+    }
+    return launched();
+}
+
+template <int C>
+int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStream_t st)
+{
+    const int chunks_per_row = dW / 16;
+    const long long chunks = (long long)batch * dH * chunks_per_row;
+    long long blocks = (chunks + kBlock - 1) / kBlock;
+    if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
+    hipLaunchKernelGGL((linear_half_u8<C>), dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                       (const uint8_t *)src, (uint8_t *)dst, dW, chunks, chunks_per_row);
+    return launched();
+}
+
+template <int BPP>
+int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                   hipStream_t st)
+{
+    const long long rows = (long long)batch * dH;
+    const Grid g = band_grid(rows, dW);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const uint8_t *)src,
+                           (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks);
+    };
+    if constexpr (BPP % 16 == 0) {
+        if (aligned(src, 16) && aligned(dst, 16)) { go(nearest_generic<BPP, 16>); return launched(); }
+    }
+    if constexpr (BPP % 4 == 0) {
+        if (aligned(src, 4) && aligned(dst, 4)) { go(nearest_generic<BPP, 4>); return launched(); }
+    }
+    go(nearest_generic<BPP, 1>);
+    return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+int resize_abi_version(void) { return MI_RESIZE_ABI_VERSION; }
+
+const char *resize_status_string(int status)
+{
+    switch (status) {
+    case MI_RESIZE_OK: return "ok";
+    case MI_RESIZE_ERR_NULL: return "src or dst is a null pointer";
+    case MI_RESIZE_ERR_SHAPE:
+        return "a size is out of range (need 1 <= H, W, dst_H, dst_W <= 65535, batch >= 1, "
+               "batch*dst_H*dst_W <= 2^40)";
+    case MI_RESIZE_ERR_CHANNELS: return "channel count must be 1, 3 or 4";
+    case MI_RESIZE_ERR_DTYPE: return "dtype must be MI_RESIZE_U8 (0) or MI_RESIZE_F32 (1)";
+    case MI_RESIZE_ERR_OVERLAP: return "src and dst buffers overlap";
+    case MI_RESIZE_ERR_HIP: return "the HIP runtime refused the kernel launch";
+    default: return "unknown status";
+    }
+}
+
+int resize_linear(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                  int dst_H, int dst_W, void *stream)
+{
+    const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
+    if (rc != MI_RESIZE_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const bool generic_only = env_flag("MI_RESIZE_FORCE_GENERIC");
+    if (dtype == MI_RESIZE_U8) {
+        if (!generic_only && H == 2 * dst_H && W == 2 * dst_W && dst_W % 16 == 0 &&
+            aligned(src, 16) && aligned(dst, 16)) {
+            switch (C) {
+            case 1: return launch_half_u8<1>(src, dst, batch, dst_H, dst_W, st);
+            case 3: return launch_half_u8<3>(src, dst, batch, dst_H, dst_W, st);
+            default: return launch_half_u8<4>(src, dst, batch, dst_H, dst_W, st);
+            }
+        }
+        switch (C) {
+        case 1: return launch_linear_generic<uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
+        case 3: return launch_linear_generic<uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+        default: return launch_linear_generic<uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+        }
+    }
+    switch (C) {
+    case 1: return launch_linear_generic<float, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 3: return launch_linear_generic<float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+    default: return launch_linear_generic<float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+    }
+}
+
+int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                   int dst_H, int dst_W, void *stream)
+{
+    const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
+    if (rc != MI_RESIZE_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int bpp = C * (dtype == MI_RESIZE_U8 ? 1 : 4);
+    switch (bpp) {
+    case 1: return launch_nearest<1>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 3: return launch_nearest<3>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 4: return launch_nearest<4>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 12: return launch_nearest<12>(src, dst, batch, H, W, dst_H, dst_W, st);
+    default: return launch_nearest<16>(src, dst, batch, H, W, dst_H, dst_W, st);
+    }
+}
+
+int resize_copy_bytes(const void *src, void *dst, int64_t nbytes, void *stream)
+{
+    if (!src || !dst) return MI_RESIZE_ERR_NULL;
+    if (nbytes < 0) return MI_RESIZE_ERR_SHAPE;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (nbytes > 0 && s0 < d0 + (uintptr_t)nbytes && d0 < s0 + (uintptr_t)nbytes)
+        return MI_RESIZE_ERR_OVERLAP;
+    if (nbytes == 0) return MI_RESIZE_OK;
+    hipStream_t st = (hipStream_t)stream;
+    long long head = 0;
+    if (aligned(src, 16) && aligned(dst, 16)) {
+        const long long n16 = nbytes / 16;
+        if (n16 > 0) {
+            long long blocks = (n16 + kBlock - 1) / kBlock;
+            if (blocks > 256 * 32) blocks = 256 * 32;
+            hipLaunchKernelGGL(copy_16, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                               (const uint4 *)src, (uint4 *)dst, n16);
+            head = n16 * 16;
+        }
+    }
+    const long long rest = nbytes - head;
+    if (rest > 0) {
+        long long blocks = (rest + kBlock - 1) / kBlock;
+        if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
+        hipLaunchKernelGGL(copy_1, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                           (const uint8_t *)src + head, (uint8_t *)dst + head, rest);
+    }
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+/*
+ * mi_resize.h - C ABI of the gfx950 image-resize library (libmi_resize.so).
+ *
+ * Operations
+ *   resize_linear   linear (bilinear) interpolation, OpenCV INTER_LINEAR
+ *                   style.  Defined by "From Prototype to Performance:
+ *                   Optimizing OpenCV Resize on Volcanic GPUs" (Imagination
+ *                   blog), sections "Step 1: Build a reliable reference path"
+ *                   and "Naive resize with linear sampling" (each output pixel
+ *                   centre, coordinate + 0.5, is scaled back into the input and
+ *                   sampled with a linear filter), and by hnwysp.cn news/129086
+ *                   s2.2 (the four-neighbour weighted sum), s3.3 (the second
+ *                   neighbour is limited to the last pixel), s6.1 (clamping)
+ *                   and s6.2 (fixed point).
+ *   resize_nearest  nearest neighbour, hnwysp.cn news/129086 s2.1 (map the
+ *                   output pixel into the input and round to the nearest
+ *                   pixel) with the same half-pixel map and clamping.
+ *
+ * What is computed, per image n, output pixel (dy, dx), channel c:
+ *   - source coordinate x = (dx + 0.5) * W / dW - 0.5 (and likewise y with
+ *     H / dH), carried as an exact fraction; x0 = floor(x), u = x - x0;
+ *     neighbour columns clamp(x0, 0, W-1) and clamp(x0 + 1, 0, W-1)
+ *     ("clamp to edge"); rows the same.
+ *   - uint8: u and v are rounded half up to 11 fractional bits
+ *     (U = round(2048 u) in [0, 2048]); the result is
+ *       ((2048-V)((2048-U) p00 + U p01) + V((2048-U) p10 + U p11) + 2^21) >> 22
+ *     evaluated exactly in integers (rounded once, half up).
+ *   - float32: u = r / den computed from the exact remainder, then
+ *       t = p00 + u (p01 - p00), b = p10 + u (p11 - p10), out = t + v (b - t)
+ *     in float32 fused multiply-adds.  Agrees with the exact real-valued
+ *     bilinear value to well within 1e-5 for inputs in [0, 1].
+ *   - nearest: source column min(floor((dx + 0.5) * W / dW), W - 1) (the
+ *     half-pixel coordinate rounded half up), likewise the row; the element
+ *     bytes are copied unchanged.
+ *
+ * Layout: src is batch x H x W x C, dst is batch x dst_H x dst_W x C, both
+ * contiguous with interleaved channels (HWC per image, images back to back),
+ * same element type.  Element type: dtype MI_RESIZE_U8 (uint8_t) or
+ * MI_RESIZE_F32 (float).  C is 1, 3 or 4.
+ *
+ * Pointers: src and dst are DEVICE pointers (hipMalloc'ed memory or memory
+ * the device can access, e.g. torch CUDA tensors) owned by the caller.  The
+ * library allocates nothing, keeps no state between calls and never takes
+ * ownership.  The two byte ranges must not overlap.  Any alignment is
+ * accepted; 16-byte aligned buffers take the vectorised paths.
+ *
+ * Stream: the work is enqueued on `stream` (a hipStream_t; NULL means the
+ * null stream) and the call returns without waiting.  The caller synchronises
+ * before reading dst.  Calls are re-entrant and thread safe.
+ *
+ * Errors: every argument is checked before anything is enqueued; on a bad
+ * argument the call returns a non-zero status, enqueues nothing and leaves
+ * dst untouched.  A failed kernel launch returns MI_RESIZE_ERR_HIP.  A fault
+ * during execution (e.g. a host pointer passed as src) is reported by the HIP
+ * runtime at the caller's next synchronisation.
+ *
+ * Limits: 1 <= H, W, dst_H, dst_W <= 65535; batch >= 1;
+ * batch * dst_H * dst_W <= 2^40.
+ */
+#ifndef MI_RESIZE_H
+#define MI_RESIZE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_RESIZE_ABI_VERSION 1
+
+enum mi_resize_dtype {
+    MI_RESIZE_U8 = 0,   /* uint8_t elements  */
+    MI_RESIZE_F32 = 1   /* float32 elements  */
+};
+
+enum mi_resize_status {
+    MI_RESIZE_OK = 0,
+    MI_RESIZE_ERR_NULL = 1,      /* src or dst is NULL                        */
+    MI_RESIZE_ERR_SHAPE = 2,     /* a size is out of the limits above         */
+    MI_RESIZE_ERR_CHANNELS = 3,  /* C is not 1, 3 or 4                        */
+    MI_RESIZE_ERR_DTYPE = 4,     /* dtype is not MI_RESIZE_U8 / MI_RESIZE_F32 */
+    MI_RESIZE_ERR_OVERLAP = 5,   /* src and dst byte ranges overlap           */
+    MI_RESIZE_ERR_HIP = 6        /* the HIP runtime refused the launch        */
+};
+
+/* Linear (bilinear) resize; see the header comment for the exact result. */
+int resize_linear(const void *src, void *dst, int batch, int H, int W, int C,
+                  int dtype, int dst_H, int dst_W, void *stream);
+
+/* Nearest-neighbour resize (half-pixel centres, rounding half up). */
+int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C,
+                   int dtype, int dst_H, int dst_W, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *resize_status_string(int status);
+
+/* MI_RESIZE_ABI_VERSION of the built library. */
+int resize_abi_version(void);
+
+/*
+ * Bandwidth calibration: copy nbytes from src to dst (device pointers, no
+ * overlap) with 16-byte loads and stores, enqueued on `stream`.  This is the
+ * plain copy against which measured HBM traffic and bandwidth are scaled; it
+ * is the counterpart of the 1:1 copy kernel that "From Prototype to
+ * Performance" (section "Baseline: simple 1:1 copy behavior") uses as its
+ * rough ceiling.  Returns a status code as above.
+ */
+int resize_copy_bytes(const void *src, void *dst, int64_t nbytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_RESIZE_H */

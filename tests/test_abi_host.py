@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+its header declares, and rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel launch: each one fails argument validation,
+which runs on the host before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bilinear_image_resize_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi_resize.h")
+
+FAKE_SRC = 0x10000000
+FAKE_DST = 0x20000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("resize_linear", "resize_nearest", "resize_status_string",
+              "resize_abi_version", "resize_copy_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(R.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert R.resize_abi_version() == 1
+    for code in range(7):
+        s = R.resize_status_string(code)
+        assert isinstance(s, str) and s
+    assert R.resize_status_string(99) == "unknown status"
+
+
+def call(name, src=FAKE_SRC, dst=FAKE_DST, batch=1, H=8, W=8, C=3, dtype=0, dH=4, dW=4):
+    return getattr(R._load(), name)(src, dst, batch, H, W, C, dtype, dH, dW, None)
+
+
+@pytest.mark.parametrize("name", ["resize_linear", "resize_nearest"])
+def test_argument_validation(name):
+    assert call(name, src=None) == 1
+    assert call(name, dst=None) == 1
+    for kw in ({"batch": 0}, {"H": 0}, {"W": -1}, {"dH": 0}, {"dW": 0},
+               {"H": 65536}, {"dW": 70000}, {"batch": 1 << 30, "dH": 65535, "dW": 65535}):
+        assert call(name, **kw) == 2, kw
+    for c in (0, 2, 5, 16):
+        assert call(name, C=c) == 3
+    for d in (-1, 2, 7):
+        assert call(name, dtype=d) == 4
+    # dst inside src, src inside dst, partial overlaps
+    assert call(name, src=FAKE_SRC, dst=FAKE_SRC + 5) == 5
+    assert call(name, src=FAKE_SRC + 5, dst=FAKE_SRC) == 5
+    assert call(name, src=FAKE_SRC, dst=FAKE_SRC + 8 * 8 * 3 - 1) == 5
+    # checks come in a fixed order: null before dtype before channels before shape
+    assert call(name, src=None, C=7, dtype=9) == 1
+    assert call(name, C=7, dtype=9) == 4
+    assert call(name, C=7, H=0) == 3
+
+
+def test_copy_validation():
+    lib = R._load()
+    assert lib.resize_copy_bytes(None, FAKE_DST, 16, None) == 1
+    assert lib.resize_copy_bytes(FAKE_SRC, FAKE_DST, -1, None) == 2
+    assert lib.resize_copy_bytes(FAKE_SRC, FAKE_SRC + 8, 16, None) == 5
+    assert lib.resize_copy_bytes(FAKE_SRC, FAKE_DST, 0, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(R, "_lib", None)
+    monkeypatch.setattr(R, "_LIB_PATH", "/nonexistent/libmi_resize.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        R.resize_abi_version()

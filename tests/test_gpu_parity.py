@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+uint8 results must be bit-exact; float32 results within 1e-5 absolute for
+inputs in [0, 1] (the tolerance the resize is specified to).  Every call goes
+through the C ABI (via the ctypes binding).  Each case prints its name before
+its GPU work so a failing run names the case.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bilinear_image_resize_amd as R
+import oracle
+from bilinear_image_resize_amd.workloads import WORKLOADS, make_source, random_image
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    R._load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_gpu(src_np, dH, dW, mode="linear", stream=None):
+    src = torch.from_numpy(src_np).cuda()
+    N, H, W, C = src.shape
+    dst = torch.empty((N, dH, dW, C), dtype=src.dtype, device="cuda")
+    if mode == "linear":
+        R.resize_linear(src, dst, stream=stream)
+    else:
+        R.resize_nearest(src, dst, stream=stream)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy()
+
+
+def run_oracle(src_np, dH, dW, mode="linear"):
+    if mode == "linear":
+        return oracle.resize_linear(src_np, dH, dW)
+    return oracle.resize_nearest(src_np, dH, dW)
+
+
+def assert_parity(got, want, what):
+    assert got.shape == want.shape, what
+    if want.dtype == np.uint8 or want.dtype != np.float32:
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, "%s: %d mismatches, first at %s (got %s want %s)" % (
+            what, len(bad), tuple(bad[0]), got[tuple(bad[0])], want[tuple(bad[0])])
+    else:
+        err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+        assert np.isfinite(got).all(), what
+        assert err.max() <= F32_TOL, "%s: max abs err %g at %s" % (
+            what, err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
+# --------------------------------------------------------------------------
+# the five workloads at their full sizes, in the launch configuration the
+# benchmark times (default dispatch), and again forced onto the generic kernel
+# --------------------------------------------------------------------------
+CASES = [(w.name, m) for w in WORKLOADS.values() for m in w.modes]
+
+
+@pytest.mark.parametrize("name,mode", CASES)
+def test_workload_full_size(name, mode):
+    w = WORKLOADS[name]
+    say("case workload=%s mode=%s src=%s dst=%s" % (name, mode, w.src_shape, w.dst_shape))
+    s = make_source(w)
+    assert_parity(run_gpu(s, w.dH, w.dW, mode), run_oracle(s, w.dH, w.dW, mode),
+                  "%s/%s" % (name, mode))
+
+
+@pytest.mark.parametrize("name", ["small", "4k", "up2x"])
+def test_workload_generic_kernel(name, monkeypatch):
+    w = WORKLOADS[name]
+    monkeypatch.setenv("MI_RESIZE_FORCE_GENERIC", "1")
+    say("case workload=%s generic kernel" % name)
+    s = make_source(w)
+    assert_parity(run_gpu(s, w.dH, w.dW), run_oracle(s, w.dH, w.dW), name + "/generic")
+
+
+# --------------------------------------------------------------------------
+# randomised shapes: dims 1..300, scales ~0.1..8, C in {1,3,4}, N in {1,3}
+# --------------------------------------------------------------------------
+def random_case(r):
+    N = int(r.choice([1, 3]))
+    C = int(r.choice([1, 3, 4]))
+    H, W = (int(v) for v in r.integers(1, 301, size=2))
+    sy, sx = np.exp(r.uniform(np.log(0.1), np.log(8.0), size=2))
+    dH = int(min(max(1, round(H * sy)), 600))
+    dW = int(min(max(1, round(W * sx)), 600))
+    return N, H, W, C, dH, dW
+
+
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+@pytest.mark.parametrize("mode", ["linear", "nearest"])
+def test_random_shapes(dtype, mode):
+    r = np.random.default_rng(2024 + (dtype == "f32") + 2 * (mode == "nearest"))
+    for i in range(60):
+        N, H, W, C, dH, dW = random_case(r)
+        say("case random %s %s #%d N=%d H=%d W=%d C=%d -> %dx%d" % (dtype, mode, i, N, H, W, C, dH, dW))
+        s = random_image(r, (N, H, W, C), dtype)
+        assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
+                      "random #%d %s" % (i, (N, H, W, C, dH, dW)))
+
+
+# --------------------------------------------------------------------------
+# exact 2:1 downscale (its own kernel) for every channel count, ragged batch,
+# and the shapes just off its conditions (which take the generic kernel)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("C", [1, 3, 4])
+def test_half_downscale_shapes(C):
+    r = np.random.default_rng(77 + C)
+    for (N, dH, dW) in ((1, 1, 16), (3, 5, 32), (2, 17, 48), (1, 64, 1920), (5, 3, 16 * 37),
+                        (1, 9, 15), (2, 4, 17), (1, 1, 1), (1, 7, 31)):
+        say("case half C=%d N=%d dst=%dx%d" % (C, N, dH, dW))
+        s = random_image(r, (N, 2 * dH, 2 * dW, C), "u8")
+        assert_parity(run_gpu(s, dH, dW), run_oracle(s, dH, dW), "half %s" % ((C, N, dH, dW),))
+
+
+# --------------------------------------------------------------------------
+# degenerate and extreme shapes
+# --------------------------------------------------------------------------
+EDGE = [
+    (1, 1, 1, 1, 1, 1), (1, 1, 1, 3, 7, 9), (1, 5, 7, 4, 1, 1), (1, 1, 300, 3, 1, 41),
+    (1, 300, 1, 1, 53, 1), (2, 1, 1, 4, 33, 65), (1, 3, 3, 1, 600, 600), (1, 600, 600, 3, 2, 3),
+    (1, 2, 65535, 1, 3, 40000), (1, 40000, 2, 1, 65535, 3), (1, 1, 65535, 4, 1, 65535),
+    (4, 13, 17, 3, 13, 17), (1, 8, 8, 3, 8, 16), (1, 8, 8, 3, 16, 8),
+    (7, 31, 33, 3, 61, 67), (1, 1000, 10, 1, 3, 999),
+]
+
+
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+@pytest.mark.parametrize("mode", ["linear", "nearest"])
+def test_edge_shapes(dtype, mode):
+    r = np.random.default_rng(99)
+    for (N, H, W, C, dH, dW) in EDGE:
+        say("case edge %s %s %s" % (dtype, mode, (N, H, W, C, dH, dW)))
+        s = random_image(r, (N, H, W, C), dtype)
+        assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
+                      "edge %s" % ((N, H, W, C, dH, dW),))
+
+
+def test_batch_of_tiny_images():
+    r = np.random.default_rng(5)
+    s = random_image(r, (1000, 3, 2, 3), "u8")
+    say("case tiny batch 1000x3x2x3 -> 5x7")
+    assert_parity(run_gpu(s, 5, 7), run_oracle(s, 5, 7), "tiny batch")
+
+
+# --------------------------------------------------------------------------
+# misaligned buffers take the scalar paths; results must not change
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+@pytest.mark.parametrize("mode", ["linear", "nearest"])
+def test_misaligned_buffers(dtype, mode):
+    r = np.random.default_rng(11)
+    es = 1 if dtype == "u8" else 4
+    for (N, H, W, C, dH, dW) in ((1, 64, 64, 4, 32, 32), (2, 40, 64, 3, 20, 32), (1, 33, 47, 1, 70, 20)):
+        for off in ((1, 3) if dtype == "u8" else (1, 2)):
+            say("case misaligned %s %s off=%d %s" % (dtype, mode, off, (N, H, W, C, dH, dW)))
+            s_np = random_image(r, (N, H, W, C), dtype)
+            tdt = torch.uint8 if dtype == "u8" else torch.float32
+            n_src, n_dst = s_np.size, N * dH * dW * C
+            src_buf = torch.empty(n_src + 8, dtype=tdt, device="cuda")
+            dst_buf = torch.empty(n_dst + 8, dtype=tdt, device="cuda")
+            src = src_buf[off:off + n_src].view(N, H, W, C)
+            dst = dst_buf[off:off + n_dst].view(N, dH, dW, C)
+            assert src.data_ptr() % 16 == off * es
+            src.copy_(torch.from_numpy(s_np))
+            (R.resize_linear if mode == "linear" else R.resize_nearest)(src, dst)
+            torch.cuda.synchronize()
+            assert_parity(dst.cpu().numpy(), run_oracle(s_np, dH, dW, mode), "misaligned")
+
+
+# --------------------------------------------------------------------------
+# nothing is written outside dst: canary bytes on both sides
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_guard_bands(dtype):
+    r = np.random.default_rng(12)
+    tdt = torch.uint8 if dtype == "u8" else torch.float32
+    pad = 4096
+    for (N, H, W, C, dH, dW) in ((1, 100, 64, 3, 50, 32), (2, 37, 53, 4, 71, 29),
+                                 (1, 64, 96, 1, 32, 48), (3, 16, 16, 3, 8, 8)):
+        for mode in ("linear", "nearest"):
+            say("case guard %s %s %s" % (dtype, mode, (N, H, W, C, dH, dW)))
+            s_np = random_image(r, (N, H, W, C), dtype)
+            n = N * dH * dW * C
+            buf = torch.full((n + 2 * pad,), 77, dtype=tdt, device="cuda")
+            dst = buf[pad:pad + n].view(N, dH, dW, C)
+            (R.resize_linear if mode == "linear" else R.resize_nearest)(
+                torch.from_numpy(s_np).cuda(), dst)
+            torch.cuda.synchronize()
+            host = buf.cpu().numpy()
+            assert (host[:pad] == 77).all() and (host[pad + n:] == 77).all()
+            assert_parity(host[pad:pad + n].reshape(N, dH, dW, C),
+                          run_oracle(s_np, dH, dW, mode), "guard")
+
+
+# --------------------------------------------------------------------------
+# a non-default stream, and HWC (unbatched) tensors through resize()
+# --------------------------------------------------------------------------
+def test_side_stream_and_hwc():
+    r = np.random.default_rng(13)
+    s_np = random_image(r, (1, 480, 640, 3), "u8")
+    st = torch.cuda.Stream()
+    src = torch.from_numpy(s_np[0]).cuda()
+    torch.cuda.synchronize()
+    say("case side stream")
+    with torch.cuda.stream(st):
+        out = R.resize(src, (224, 224))
+    st.synchronize()
+    assert out.shape == (224, 224, 3)
+    assert_parity(out.cpu().numpy()[None], oracle.resize_linear(s_np, 224, 224), "stream")
+    out2 = R.resize(src, scale=0.5, mode="nearest")
+    torch.cuda.synchronize()
+    assert out2.shape == (240, 320, 3)
+    assert_parity(out2.cpu().numpy()[None], oracle.resize_nearest(s_np, 240, 320), "scale")
+
+
+def test_binding_rejects_bad_tensors():
+    with pytest.raises(ValueError):
+        R.resize(torch.zeros(4, 4, 3, dtype=torch.uint8), (2, 2))          # host tensor
+    with pytest.raises(TypeError):
+        R.resize(torch.zeros(4, 4, 3, dtype=torch.int32, device="cuda"), (2, 2))
+    with pytest.raises(R.ResizeError):
+        R.resize(torch.zeros(4, 4, 2, dtype=torch.uint8, device="cuda"), (2, 2))  # C=2
+    with pytest.raises(ValueError):
+        R.resize(torch.zeros(4, 4, 3, dtype=torch.uint8, device="cuda")[:, ::2], (2, 2))
+
+
+def test_copy_bytes():
+    for n in (16, 1000, 4096 * 16 + 5, 3 << 20):
+        say("case copy %d" % n)
+        a = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+        b = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        R.resize_copy_bytes(a, b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
