@@ -91,16 +91,26 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
     return launched();
 }
 
+constexpr long long kMaxGridY = 65535;
+
 template <int C>
 int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStream_t st)
 {
-    const int chunks_per_row = dW / 16;
-    const long long chunks = (long long)batch * dH * chunks_per_row;
-    long long blocks = (chunks + kBlock - 1) / kBlock;
-    if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
-    hipLaunchKernelGGL((linear_half_u8<C>), dim3((unsigned)blocks), dim3(kBlock), 0, st,
-                       (const uint8_t *)src, (uint8_t *)dst, dW, chunks, chunks_per_row);
+    const int chunks_per_row = dW / HalfShape<C>::PX;
+    const long long rows = (long long)batch * dH;
+    const dim3 grid((chunks_per_row + kHalfBlock - 1) / kHalfBlock,
+                    (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
+    hipLaunchKernelGGL((linear_half_u8<C>), grid, dim3(kHalfBlock), 0, st, (const uint8_t *)src,
+                       (uint8_t *)dst, dW, rows, chunks_per_row);
     return launched();
+}
+
+// Exact 2:1 uint8 downscale whose rows split into whole lanes.
+bool half_path_fits(int C, int H, int W, int dH, int dW, const void *src, const void *dst)
+{
+    if (H != 2 * dH || W != 2 * dW || !aligned(src, 16) || !aligned(dst, 16)) return false;
+    const int px = C == 1 ? HalfShape<1>::PX : C == 3 ? HalfShape<3>::PX : HalfShape<4>::PX;
+    return dW % px == 0;
 }
 
 template <int BPP>
@@ -153,8 +163,7 @@ int resize_linear(const void *src, void *dst, int batch, int H, int W, int C, in
     hipStream_t st = (hipStream_t)stream;
     const bool generic_only = env_flag("MI_RESIZE_FORCE_GENERIC");
     if (dtype == MI_RESIZE_U8) {
-        if (!generic_only && H == 2 * dst_H && W == 2 * dst_W && dst_W % 16 == 0 &&
-            aligned(src, 16) && aligned(dst, 16)) {
+        if (!generic_only && half_path_fits(C, H, W, dst_H, dst_W, src, dst)) {
             switch (C) {
             case 1: return launch_half_u8<1>(src, dst, batch, dst_H, dst_W, st);
             case 3: return launch_half_u8<3>(src, dst, batch, dst_H, dst_W, st);

@@ -193,46 +193,62 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // general formula reduces, bit for bit, to the rounded 2x2 mean
 // (a + b + c + d + 2) >> 2.  No tap is ever clamped.
 //
-// A lane produces 16 consecutive output pixels (grid-stride over chunks) (16 C bytes, C 16-byte
-// stores) from 32 source pixels of two rows (2 x 2C 16-byte loads).  Requires
-// dW % 16 == 0 and 16-byte aligned src and dst (then every row start is
-// 16-byte aligned too).  Global source row of output row g is 2g, because
-// H = 2 dH makes n H + 2 dy = 2 (n dH + dy).
+// A lane owns PX consecutive output pixels of one row: it loads 2 PX C bytes
+// from each of the two source rows and stores PX C bytes, with PX chosen so
+// that a lane moves 32-48 source bytes (C = 1: 8 px, 16 B per row; C = 3:
+// 4 px, 24 B per row; C = 4: 2 px, 16 B per row).  Measured on the 4K RGB
+// frame, lanes this small beat 8- and 16-pixel lanes: more lanes in flight
+// hide more HBM latency, and a lane's loads of both rows go out together.
+// Grid: x = 64-lane workgroups across a row, y = output rows (stride
+// gridDim.y).  Needs dW % PX == 0 and 16-byte aligned src / dst; then every
+// lane's accesses are naturally aligned.  Output row g reads source rows 2g
+// and 2g + 1 of the flattened N*H rows, because H = 2 dH.
 // --------------------------------------------------------------------------
-template <int C>
-__global__ __launch_bounds__(kBlock) void linear_half_u8(
-    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW,
-    long long chunks_total, int chunks_per_row)
-{
-    const size_t src_row = (size_t)2 * dW * C;          // bytes per source row
-    const long long stride = (long long)gridDim.x * kBlock;
-    for (long long t = (long long)blockIdx.x * kBlock + threadIdx.x; t < chunks_total;
-         t += stride) {
-        const long long g = t / chunks_per_row;
-        const int j = (int)(t - g * chunks_per_row);
-        const uint8_t *s0 = src + (size_t)(2 * g) * src_row + (size_t)j * 32 * C;
-        const uint8_t *s1 = s0 + src_row;
-        uint8_t *o = dst + (size_t)g * dW * C + (size_t)j * 16 * C;
+template <int C> struct HalfShape;
+template <> struct HalfShape<1> { static constexpr int PX = 8; using LV = uint4; using SV = uint2; };
+template <> struct HalfShape<3> { static constexpr int PX = 4; using LV = uint2; using SV = uint32_t; };
+template <> struct HalfShape<4> { static constexpr int PX = 2; using LV = uint4; using SV = uint2; };
 
-        uint4 a[2 * C], b[2 * C];
+constexpr int kHalfBlock = 64;
+
+template <int C>
+__global__ __launch_bounds__(kHalfBlock) void linear_half_u8(
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows,
+    int chunks_per_row)
+{
+    using S = HalfShape<C>;
+    using LV = typename S::LV;
+    using SV = typename S::SV;
+    constexpr int INB = 2 * S::PX * C;            // source bytes per row per lane
+    constexpr int NIN = INB / (int)sizeof(LV);
+    constexpr int NOUT = S::PX * C;               // output bytes per lane
+    constexpr int NST = NOUT / (int)sizeof(SV);
+    const int j = blockIdx.x * kHalfBlock + threadIdx.x;
+    if (j >= chunks_per_row) return;
+    const size_t src_row = (size_t)2 * dW * C;
+    const size_t dst_row = (size_t)dW * C;
+    for (long long g = blockIdx.y; g < rows; g += gridDim.y) {
+        const LV *s0 = (const LV *)(src + (size_t)(2 * g) * src_row + (size_t)j * INB);
+        const LV *s1 = (const LV *)((const uint8_t *)s0 + src_row);
+        LV a[NIN], b[NIN];
 #pragma unroll
-        for (int k = 0; k < 2 * C; ++k) {
-            a[k] = ((const uint4 *)s0)[k];
-            b[k] = ((const uint4 *)s1)[k];
+        for (int k = 0; k < NIN; ++k) {
+            a[k] = s0[k];
+            b[k] = s1[k];
         }
         const uint8_t *pa = (const uint8_t *)a;
         const uint8_t *pb = (const uint8_t *)b;
-        uint4 res[C];
-        uint8_t *pr = (uint8_t *)res;
+        SV r[NST];
+        uint8_t *pr = (uint8_t *)r;
 #pragma unroll
-        for (int k = 0; k < 16 * C; ++k) {
-            const int x = k / C, c = k - (k / C) * C;
-            const int p = 2 * C * x + c;
+        for (int k = 0; k < NOUT; ++k) {
+            const int p = 2 * k - k % C;          // first source byte of output byte k
             const unsigned s = (unsigned)pa[p] + pa[p + C] + pb[p] + pb[p + C] + 2u;
             pr[k] = (uint8_t)(s >> 2);
         }
+        SV *o = (SV *)(dst + (size_t)g * dst_row + (size_t)j * NOUT);
 #pragma unroll
-        for (int k = 0; k < C; ++k) ((uint4 *)o)[k] = res[k];
+        for (int k = 0; k < NST; ++k) o[k] = r[k];
     }
 }
 
