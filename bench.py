@@ -48,7 +48,42 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="instead of resizing, time the plain 16-byte copy kernel on BYTES "
+                        "bytes (cold rotation); used to scale HBM traffic counters")
     return p.parse_args()
+
+
+def copy_calibration(args):
+    """Run resize_copy_bytes over `args.copy_calibration` bytes per launch,
+    rotating over enough buffers to defeat the Infinity Cache."""
+    import torch
+
+    import bilinear_image_resize_amd as R
+
+    n = args.copy_calibration
+    dev = torch.device("cuda:0")
+    pairs = max(2, -(-2 * INFINITY_CACHE_BYTES // (2 * n)))
+    bufs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(k & 255),
+             torch.empty(n, dtype=torch.uint8, device=dev)) for k in range(pairs)]
+    lib = R._load()
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    ptrs = [(a.data_ptr(), b.data_ptr()) for a, b in bufs]
+    for i in range(args.warmup):
+        lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        rc = lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+        if rc:
+            raise R.ResizeError(rc, "resize_copy_bytes")
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({"copy_bytes": n, "pairs": pairs, "kernel_us": round(us, 3),
+                      "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, src_np, mode, budget_s):
@@ -96,6 +131,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
 
     import numpy as np
     import torch

@@ -25,10 +25,18 @@ constexpr long long kMaxStrideBlocks = 65536;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-bool env_flag(const char *name)
+// Kernel family override for testing: MI_RESIZE_PATH=rowseg skips the
+// scale-specific fast paths, MI_RESIZE_PATH=direct uses only the
+// direct-gather kernels.  Unset (or anything else): automatic choice.
+enum class Path { Auto, RowSeg, Direct };
+
+Path path_override()
 {
-    const char *v = getenv(name);
-    return v && v[0] && strcmp(v, "0") != 0;
+    const char *v = getenv("MI_RESIZE_PATH");
+    if (!v) return Path::Auto;
+    if (strcmp(v, "rowseg") == 0) return Path::RowSeg;
+    if (strcmp(v, "direct") == 0) return Path::Direct;
+    return Path::Auto;
 }
 
 int check_args(const void *src, const void *dst, int batch, int H, int W, int C, int dtype,
@@ -45,6 +53,7 @@ int check_args(const void *src, const void *dst, int batch, int H, int W, int C,
     const uintptr_t s1 = s0 + (size_t)batch * H * W * C * es;
     const uintptr_t d1 = d0 + (size_t)batch * dH * dW * C * es;
     if (s0 < d1 && d0 < s1) return MI_RESIZE_ERR_OVERLAP;
+    if (es == 4 && (!aligned(src, 4) || !aligned(dst, 4))) return MI_RESIZE_ERR_ALIGN;
     return MI_RESIZE_OK;
 }
 
@@ -105,6 +114,80 @@ int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStr
     return launched();
 }
 
+// LDS bytes one row-segment workgroup may use (two slots).  Beyond it the
+// segment is too wide (strong downscale) and the direct kernels run instead;
+// at 16 KiB a CU still holds 10 such one-wave workgroups.
+constexpr int kSegLdsBudget = 16 * 1024;
+// One-wave workgroups a row-segment launch aims for: 32 per CU on 256 CUs.
+constexpr long long kSegTargetBlocks = 8192;
+// Below this many output pixels the launch is latency-bound and the direct
+// kernels (no staging round trip, no per-lane column table of PX entries)
+// finish first.
+constexpr long long kSmallOutPixels = 1LL << 16;
+
+struct SegPlan {
+    dim3 grid;
+    int rows_per_block;
+    int seg_cap;
+};
+
+// Bytes per LDS slot for the widest segment: the source columns touched by
+// kernel-side output columns wx0..wx1 span at most (wx1 - wx0) * W / dW + 3
+// columns (taps on both sides plus rounding), plus 15 bytes of misalignment
+// and the slack a two-tap read may run past the last staged pixel.
+bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, SegPlan &pl)
+{
+    const long long cols = (long long)kSegLanes * px;
+    long long span = ((cols - 1) * W) / dW + 3;
+    if (span > W) span = W;
+    const long long cap = ((span * pixel_bytes + 15 + kSegReadSlack + 15) / 16) * 16;
+    if (2 * cap > kSegLdsBudget) return false;
+    pl.seg_cap = (int)cap;
+    const long long gx = (dW + cols - 1) / cols;
+    long long rpb = (rows * gx + kSegTargetBlocks - 1) / kSegTargetBlocks;
+    if (rpb < 1) rpb = 1;
+    pl.rows_per_block = (int)rpb;
+    pl.grid = dim3((unsigned)gx, (unsigned)((rows + rpb - 1) / rpb));
+    return true;
+}
+
+template <typename T, int C, bool NEAREST>
+bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                hipStream_t st, int &rc)
+{
+    const long long rows = (long long)batch * dH;
+    SegPlan pl;
+    if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, pl)) return false;
+    hipLaunchKernelGGL((rowseg<T, C, NEAREST>), pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st,
+                       (const T *)src, (T *)dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
+                       (long long)batch * H * W * C);
+    rc = launched();
+    return true;
+}
+
+template <int C, bool NEAREST>
+int launch_up2_u8(const void *src, void *dst, int batch, int H, int W, hipStream_t st)
+{
+    const int chunks_per_row = W / Up2Shape<C>::S;
+    const long long rows = (long long)batch * H;
+    const dim3 grid((chunks_per_row + 63) / 64, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
+    if constexpr (NEAREST)
+        hipLaunchKernelGGL((nearest_up2_u8<C>), grid, dim3(64), 0, st, (const uint8_t *)src,
+                           (uint8_t *)dst, H, W, rows, chunks_per_row);
+    else
+        hipLaunchKernelGGL((linear_up2_u8<C>), grid, dim3(64), 0, st, (const uint8_t *)src,
+                           (uint8_t *)dst, H, W, rows, chunks_per_row);
+    return launched();
+}
+
+// Exact 2x uint8 upscale whose rows split into whole, 16-byte aligned lanes.
+bool up2_path_fits(int C, int H, int W, int dH, int dW, const void *src, const void *dst)
+{
+    if (dH != 2 * H || dW != 2 * W || !aligned(src, 16) || !aligned(dst, 16)) return false;
+    const int S = C == 4 ? Up2Shape<4>::S : Up2Shape<1>::S;
+    return W % S == 0 && ((long long)W * C) % 16 == 0;
+}
+
 // Exact 2:1 uint8 downscale whose rows split into whole lanes.
 bool half_path_fits(int C, int H, int W, int dH, int dW, const void *src, const void *dst)
 {
@@ -133,6 +216,40 @@ int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, 
     return launched();
 }
 
+template <typename T, int C>
+int linear_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                    hipStream_t st)
+{
+    const Path path = path_override();
+    if constexpr (sizeof(T) == 1) {
+        if (path == Path::Auto && half_path_fits(C, H, W, dH, dW, src, dst))
+            return launch_half_u8<C>(src, dst, batch, dH, dW, st);
+        if (path == Path::Auto && up2_path_fits(C, H, W, dH, dW, src, dst))
+            return launch_up2_u8<C, false>(src, dst, batch, H, W, st);
+    }
+    int rc;
+    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    if (path == Path::RowSeg || (path == Path::Auto && !small))
+        if (try_rowseg<T, C, false>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
+    return launch_linear_generic<T, C>(src, dst, batch, H, W, dH, dW, st);
+}
+
+template <int BPP, typename T, int C>
+int nearest_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                     hipStream_t st)
+{
+    const Path path = path_override();
+    if constexpr (sizeof(T) == 1) {
+        if (path == Path::Auto && up2_path_fits(C, H, W, dH, dW, src, dst))
+            return launch_up2_u8<C, true>(src, dst, batch, H, W, st);
+    }
+    int rc;
+    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    if (path == Path::RowSeg || (path == Path::Auto && !small))
+        if (try_rowseg<T, C, true>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
+    return launch_nearest<BPP>(src, dst, batch, H, W, dH, dW, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,6 +268,7 @@ const char *resize_status_string(int status)
     case MI_RESIZE_ERR_DTYPE: return "dtype must be MI_RESIZE_U8 (0) or MI_RESIZE_F32 (1)";
     case MI_RESIZE_ERR_OVERLAP: return "src and dst buffers overlap";
     case MI_RESIZE_ERR_HIP: return "the HIP runtime refused the kernel launch";
+    case MI_RESIZE_ERR_ALIGN: return "float32 src and dst must be 4-byte aligned";
     default: return "unknown status";
     }
 }
@@ -161,25 +279,17 @@ int resize_linear(const void *src, void *dst, int batch, int H, int W, int C, in
     const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
     if (rc != MI_RESIZE_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
-    const bool generic_only = env_flag("MI_RESIZE_FORCE_GENERIC");
     if (dtype == MI_RESIZE_U8) {
-        if (!generic_only && half_path_fits(C, H, W, dst_H, dst_W, src, dst)) {
-            switch (C) {
-            case 1: return launch_half_u8<1>(src, dst, batch, dst_H, dst_W, st);
-            case 3: return launch_half_u8<3>(src, dst, batch, dst_H, dst_W, st);
-            default: return launch_half_u8<4>(src, dst, batch, dst_H, dst_W, st);
-            }
-        }
         switch (C) {
-        case 1: return launch_linear_generic<uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
-        case 3: return launch_linear_generic<uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
-        default: return launch_linear_generic<uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+        case 1: return linear_dispatch<uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
+        case 3: return linear_dispatch<uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+        default: return linear_dispatch<uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
         }
     }
     switch (C) {
-    case 1: return launch_linear_generic<float, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
-    case 3: return launch_linear_generic<float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
-    default: return launch_linear_generic<float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 1: return linear_dispatch<float, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 3: return linear_dispatch<float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+    default: return linear_dispatch<float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
     }
 }
 
@@ -189,13 +299,17 @@ int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C, i
     const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
     if (rc != MI_RESIZE_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
-    const int bpp = C * (dtype == MI_RESIZE_U8 ? 1 : 4);
-    switch (bpp) {
-    case 1: return launch_nearest<1>(src, dst, batch, H, W, dst_H, dst_W, st);
-    case 3: return launch_nearest<3>(src, dst, batch, H, W, dst_H, dst_W, st);
-    case 4: return launch_nearest<4>(src, dst, batch, H, W, dst_H, dst_W, st);
-    case 12: return launch_nearest<12>(src, dst, batch, H, W, dst_H, dst_W, st);
-    default: return launch_nearest<16>(src, dst, batch, H, W, dst_H, dst_W, st);
+    if (dtype == MI_RESIZE_U8) {
+        switch (C) {
+        case 1: return nearest_dispatch<1, uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
+        case 3: return nearest_dispatch<3, uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+        default: return nearest_dispatch<4, uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+        }
+    }
+    switch (C) {
+    case 1: return nearest_dispatch<4, float, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 3: return nearest_dispatch<12, float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+    default: return nearest_dispatch<16, float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
     }
 }
 

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mirsz {
 
 constexpr int kBlock = 256;   // 4 wave64 per workgroup
@@ -253,6 +255,137 @@ __global__ __launch_bounds__(kHalfBlock) void linear_half_u8(
 }
 
 // --------------------------------------------------------------------------
+// Exact 2x upscale of uint8 (dH = 2 H, dW = 2 W).  Output column 2k + 1 sits
+// at source coordinate k + 1/4 and column 2k + 2 at k + 3/4, so the 11-bit
+// weights are exactly 512 and 1536 and the general formula reduces, bit for
+// bit, to (sum of k_ij p_ij + 8) >> 4 with k_ij in {9, 3, 3, 1}.  Edge taps
+// clamp to the first / last pixel, which the kernel reproduces by
+// replicating them (a clamped tap pair is one pixel with weight 16).
+//
+// A lane owns S consecutive source pixels of one source row j and writes
+// output rows 2j and 2j + 1, columns [2 S m, 2 S m + 2 S): it reads source
+// rows j - 1, j, j + 1 (clamped) over pixels -1 .. S (the outer two clamped),
+// forms the horizontal 1:3 / 3:1 sums per row, then the vertical ones.
+// Needs W % S == 0, W * C % 16 == 0 and 16-byte aligned buffers.
+// Grid: x = 64-lane workgroups across a row, y = source rows (stride
+// gridDim.y) of the flattened N * H rows.
+// --------------------------------------------------------------------------
+template <int C> struct Up2Shape { static constexpr int S = C == 4 ? 8 : 16; };
+
+template <int C>
+__global__ __launch_bounds__(64) void linear_up2_u8(
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
+    long long rows, int chunks_per_row)
+{
+    constexpr int S = Up2Shape<C>::S;
+    constexpr int IN = S * C;              // bytes of one source row chunk (multiple of 16)
+    constexpr int OUT = 2 * S * C;         // bytes of one output row chunk
+    const int m = blockIdx.x * 64 + threadIdx.x;
+    if (m >= chunks_per_row) return;
+    const size_t row_bytes = (size_t)W * C;
+    const int x0 = m * S;                                  // first source pixel of the chunk
+    const int xl = x0 > 0 ? x0 - 1 : 0;                    // left neighbour (clamped)
+    const int xr = x0 + S < W ? x0 + S : W - 1;            // right neighbour (clamped)
+    for (long long t = blockIdx.y; t < rows; t += gridDim.y) {
+        const long long n = t / H;
+        const int j = (int)(t - n * H);
+        const uint8_t *img = src + (size_t)n * H * row_bytes;
+        const int jr[3] = {j > 0 ? j - 1 : 0, j, j + 1 < H ? j + 1 : H - 1};
+        // px[r][i]: row r, pixel i - 1 (i = 0 .. S + 1), channel-interleaved bytes
+        uint8_t px[3][(S + 2) * C];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const uint8_t *row = img + (size_t)jr[r] * row_bytes;
+            uint4 v[IN / 16];
+#pragma unroll
+            for (int k = 0; k < IN / 16; ++k) v[k] = ((const uint4 *)(row + (size_t)x0 * C))[k];
+            __builtin_memcpy(&px[r][C], v, IN);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                px[r][c] = row[(size_t)xl * C + c];
+                px[r][(S + 1) * C + c] = row[(size_t)xr * C + c];
+            }
+        }
+        // horizontal sums, 4x scale: even output column 2i takes pixels
+        // (i - 1, i) with weights (1, 3); odd column 2i + 1 takes (i, i + 1)
+        // with (3, 1)
+        unsigned short hs[3][2 * S * C];
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const unsigned a = px[r][i * C + c], b = px[r][(i + 1) * C + c],
+                                   d = px[r][(i + 2) * C + c];
+                    hs[r][(2 * i) * C + c] = (unsigned short)(a + 3 * b);
+                    hs[r][(2 * i + 1) * C + c] = (unsigned short)(3 * b + d);
+                }
+        uint8_t o0[OUT], o1[OUT];
+#pragma unroll
+        for (int k = 0; k < 2 * S * C; ++k) {
+            o0[k] = (uint8_t)((hs[0][k] + 3u * hs[1][k] + 8u) >> 4);   // row 2j: rows (j-1, j)
+            o1[k] = (uint8_t)((3u * hs[1][k] + hs[2][k] + 8u) >> 4);   // row 2j+1: rows (j, j+1)
+        }
+        uint8_t *d0 = dst + ((size_t)n * 2 * H + 2 * j) * (2 * row_bytes) + (size_t)x0 * 2 * C;
+        uint8_t *d1 = d0 + 2 * row_bytes;
+#pragma unroll
+        for (int k = 0; k < OUT / 16; ++k) {
+            uint4 a, b;
+            __builtin_memcpy(&a, o0 + 16 * k, 16);
+            __builtin_memcpy(&b, o1 + 16 * k, 16);
+            ((uint4 *)d0)[k] = a;
+            ((uint4 *)d1)[k] = b;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Exact 2x nearest upscale of uint8.  For dW = 2 W the rounded half-pixel
+// coordinate of output column d is floor((2d + 1) / 4) = d / 2, so the
+// output is every source pixel repeated twice in both directions.  A lane
+// reads S pixels of source row j and writes them doubled to output rows 2j
+// and 2j + 1.  Same shape rules and grid as linear_up2_u8.
+// --------------------------------------------------------------------------
+template <int C>
+__global__ __launch_bounds__(64) void nearest_up2_u8(
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
+    long long rows, int chunks_per_row)
+{
+    constexpr int S = Up2Shape<C>::S;
+    constexpr int IN = S * C;
+    constexpr int OUT = 2 * S * C;
+    const int m = blockIdx.x * 64 + threadIdx.x;
+    if (m >= chunks_per_row) return;
+    const size_t row_bytes = (size_t)W * C;
+    for (long long t = blockIdx.y; t < rows; t += gridDim.y) {
+        uint4 v[IN / 16];
+        const uint8_t *row = src + (size_t)t * row_bytes + (size_t)m * IN;
+#pragma unroll
+        for (int k = 0; k < IN / 16; ++k) v[k] = ((const uint4 *)row)[k];
+        uint8_t in[IN], out[OUT];
+        __builtin_memcpy(in, v, IN);
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                out[(2 * i) * C + c] = in[i * C + c];
+                out[(2 * i + 1) * C + c] = in[i * C + c];
+            }
+        // source row t of the flattened N*H rows feeds output rows 2t, 2t + 1
+        uint8_t *d0 = dst + (size_t)(2 * t) * (2 * row_bytes) + (size_t)m * OUT;
+        uint8_t *d1 = d0 + 2 * row_bytes;
+#pragma unroll
+        for (int k = 0; k < OUT / 16; ++k) {
+            uint4 q;
+            __builtin_memcpy(&q, out + 16 * k, 16);
+            ((uint4 *)d0)[k] = q;
+            ((uint4 *)d1)[k] = q;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
 // Nearest neighbour, any scale, any pixel size.  Same grid as
 // linear_generic.  A pixel of BPP bytes moves in units of UNIT bytes
 // (16, 4 or 1), chosen by the host from the pixel size and the alignment.
@@ -288,6 +421,275 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
 #pragma unroll
         for (int k = 0; k < K; ++k) to[k] = from[k];
         if (++dy == dH) { dy = 0; ++n; }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Row-segment kernel: any scale, linear or nearest, u8 or f32, C in {1,3,4}.
+//
+// A workgroup is one wave (64 lanes).  It owns a segment of 64 * PX
+// consecutive output columns and a band of `rows_per_block` consecutive
+// output rows.  Each lane owns PX consecutive output pixels of the segment
+// and keeps their column taps and weights in registers for the whole band.
+//
+// Per output row the wave stages the source row(s) it needs - only the
+// columns [sa, sb] its segment touches - into LDS with 16-byte loads that
+// are coalesced across lanes, then every lane gathers its taps from LDS
+// (arbitrary, scale-dependent tap positions cost LDS reads instead of
+// scattered global accesses), blends, and writes its PX * C elements with
+// one or a few vector stores.  Both taps of one source row are adjacent, so
+// one unaligned LDS read fetches them together.  Two LDS slots cache the
+// last two staged source rows, so consecutive output rows that share a
+// source row (every upscale) stage it once.
+//
+// Row taps advance incrementally from row to row: the numerator of the
+// source coordinate grows by 2H per output row, so the quotient and
+// remainder update with one compare instead of a division.
+//
+// The host sizes `seg_cap` (bytes per slot) for the widest segment plus
+// misalignment and read slack, and uses this kernel only while 2 * seg_cap
+// stays within its LDS budget; stronger downscales take the direct kernels.
+// --------------------------------------------------------------------------
+template <typename T, int C> struct SegShape;   // PX = output pixels per lane
+template <> struct SegShape<uint8_t, 1> { static constexpr int PX = 16; };
+template <> struct SegShape<uint8_t, 3> { static constexpr int PX = 4; };
+template <> struct SegShape<uint8_t, 4> { static constexpr int PX = 4; };
+template <> struct SegShape<float, 1> { static constexpr int PX = 4; };
+template <> struct SegShape<float, 3> { static constexpr int PX = 4; };
+template <> struct SegShape<float, 4> { static constexpr int PX = 2; };
+
+constexpr int kSegLanes = 64;
+constexpr int kSegReadSlack = 16;  // bytes a two-tap LDS read may run past the segment
+
+// Stage `bytes` bytes of the source starting at p0 into an LDS slot, as
+// 16-byte chunks from the 16-byte boundary at or below p0, one chunk per
+// lane per step.  Chunks that are not wholly inside [lo, hi) are copied
+// byte by byte, so nothing outside the source buffer is read.  Returns p0's
+// offset from that boundary (its position in the slot).
+__device__ __forceinline__ int stage_segment(uint8_t *slot, const uint8_t *p0, int bytes,
+                                             const uint8_t *lo, const uint8_t *hi)
+{
+    const int m = (int)((uintptr_t)p0 & 15);
+    const uint8_t *a0 = p0 - m;
+    const int n16 = (m + bytes + 15) >> 4;
+    for (int k = threadIdx.x; k < n16; k += kSegLanes) {
+        const uint8_t *q = a0 + 16 * k;
+        uint4 v;
+        if (q >= lo && q + 16 <= hi) {
+            v = *(const uint4 *)q;
+        } else {
+            uint8_t t[16];
+#pragma unroll
+            for (int b = 0; b < 16; ++b) t[b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
+            __builtin_memcpy(&v, t, 16);
+        }
+        *(uint4 *)(slot + 16 * k) = v;
+    }
+    return m;
+}
+
+// Store N elements of one lane: vectorised when the chunk is whole and
+// aligned, element by element otherwise (row ends, odd pitches).
+template <typename T, int N>
+__device__ __forceinline__ void store_chunk(T *out, const T (&v)[N], int valid)
+{
+    constexpr int BYTES = N * (int)sizeof(T);
+    if (valid == N && BYTES % 16 == 0 && ((uintptr_t)out & 15) == 0) {
+#pragma unroll
+        for (int k = 0; k < BYTES / 16; ++k) {
+            uint4 q;
+            __builtin_memcpy(&q, (const uint8_t *)v + 16 * k, 16);
+            ((uint4 *)out)[k] = q;
+        }
+    } else if (valid == N && BYTES % 4 == 0 && ((uintptr_t)out & 3) == 0) {
+#pragma unroll
+        for (int k = 0; k < BYTES / 4; ++k) {
+            uint32_t q;
+            __builtin_memcpy(&q, (const uint8_t *)v + 4 * k, 4);
+            ((uint32_t *)out)[k] = q;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if (k < valid) out[k] = v[k];
+    }
+}
+
+// Row map that steps from output row to output row without dividing.
+struct RowStepper {
+    long long q, r;        // floor and remainder of num / den for the current row
+    long long dq, dr;      // 2 n_in = dq * den + dr
+    long long den;
+    __device__ void init(int d, int n_in, int n_out)
+    {
+        den = 2LL * n_out;
+        const long long num = (long long)(2 * d + 1) * n_in - n_out;
+        q = (long long)floor((double)num / (double)den);
+        r = num - q * den;
+        if (r < 0) { q -= 1; r += den; } else if (r >= den) { q += 1; r -= den; }
+        dq = (2LL * n_in) / den;
+        dr = (2LL * n_in) - dq * den;
+    }
+    __device__ void next()
+    {
+        q += dq;
+        r += dr;
+        if (r >= den) { r -= den; q += 1; }
+    }
+};
+
+template <typename T, int C, bool NEAREST>
+__global__ __launch_bounds__(kSegLanes) void rowseg(
+    const T *__restrict__ src, T *__restrict__ dst, int H, int W, int dH, int dW,
+    long long rows_total, int rows_per_block, int seg_cap, long long src_elems)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int PX = SegShape<T, C>::PX;
+    constexpr int PB = C * (int)sizeof(T);        // bytes per pixel
+    const int lane = threadIdx.x;
+    const int wx0 = blockIdx.x * kSegLanes * PX;  // first output column of the segment
+    const int wx1 = min(wx0 + kSegLanes * PX, dW) - 1;
+    const int x0 = wx0 + lane * PX;               // this lane's first output column
+    const int valid_px = max(0, min(PX, dW - x0));
+
+    // Source columns touched by the segment, and this lane's column table:
+    // byte offset of tap a from column sa, whether tap b is the next column
+    // (it is not only where both taps clamp to the last column), and the
+    // weight of tap b.
+    int sa, sb;
+    if constexpr (NEAREST) {
+        sa = nearest_index(wx0, W, dW);
+        sb = nearest_index(wx1, W, dW);
+    } else {
+        sa = axis_tap(wx0, W, dW).a;
+        sb = axis_tap(wx1, W, dW).b;
+    }
+    int toff[PX];
+    bool tnext[PX];
+    unsigned tw[PX];
+    float twf[PX];
+#pragma unroll
+    for (int p = 0; p < PX; ++p) {
+        const int x = min(x0 + p, dW - 1);
+        if constexpr (NEAREST) {
+            toff[p] = (nearest_index(x, W, dW) - sa) * PB;
+            tnext[p] = false;
+            tw[p] = 0;
+            twf[p] = 0.f;
+        } else {
+            const Tap t = axis_tap(x, W, dW);
+            toff[p] = (t.a - sa) * PB;
+            tnext[p] = t.b != t.a;
+            if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
+            else twf[p] = weightf(t);
+        }
+    }
+    const int seg_bytes = (sb - sa + 1) * PB;
+    const uint8_t *lo = (const uint8_t *)src;
+    const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
+    const size_t row_bytes = (size_t)W * PB;
+
+    long long g = (long long)blockIdx.y * rows_per_block;
+    long long g_end = g + rows_per_block;
+    if (g_end > rows_total) g_end = rows_total;
+    long long n = g / dH;
+    int dy = (int)(g - n * dH);
+    RowStepper ys;
+    ys.init(dy, H, dH);
+    // global source row held in each LDS slot, and its offset there
+    long long held0 = -1, held1 = -1;
+    int mis0 = 0, mis1 = 0;
+
+    for (; g < g_end; ++g) {
+        int ya, yb;
+        unsigned wy1 = 0;
+        float wyf = 0.f;
+        if constexpr (NEAREST) {
+            // nearest row: floor((2dy + 1) H / (2 dH)) = floor((num + dH) / den)
+            long long k = ys.q + ((ys.r + dH) >= ys.den ? 1 : 0);
+            ya = yb = (int)(k > H - 1 ? H - 1 : (k < 0 ? 0 : k));
+        } else {
+            const long long q = ys.q;
+            ya = (int)(q < 0 ? 0 : (q > H - 1 ? H - 1 : q));
+            yb = (int)(q + 1 < 0 ? 0 : (q + 1 > H - 1 ? H - 1 : q + 1));
+            Tap t;
+            t.r = (int)ys.r;
+            t.den = (int)ys.den;
+            if constexpr (sizeof(T) == 1) wy1 = weight11(t);
+            else wyf = weightf(t);
+        }
+        const long long ra = n * H + ya, rb = n * H + yb;
+        int sa_slot = held0 == ra ? 0 : (held1 == ra ? 1 : -1);
+        int sb_slot = held0 == rb ? 0 : (held1 == rb ? 1 : -1);
+        if (sa_slot < 0) {
+            sa_slot = (sb_slot == 0) ? 1 : 0;
+            const int m = stage_segment(lds + sa_slot * seg_cap,
+                                        lo + (size_t)ra * row_bytes + (size_t)sa * PB,
+                                        seg_bytes, lo, hi);
+            if (sa_slot == 0) { held0 = ra; mis0 = m; } else { held1 = ra; mis1 = m; }
+        }
+        if (rb == ra) {
+            sb_slot = sa_slot;
+        } else if (sb_slot < 0) {
+            sb_slot = 1 - sa_slot;
+            const int m = stage_segment(lds + sb_slot * seg_cap,
+                                        lo + (size_t)rb * row_bytes + (size_t)sa * PB,
+                                        seg_bytes, lo, hi);
+            if (sb_slot == 0) { held0 = rb; mis0 = m; } else { held1 = rb; mis1 = m; }
+        }
+        __syncthreads();
+
+        const uint8_t *la = lds + sa_slot * seg_cap + (sa_slot == 0 ? mis0 : mis1);
+        const uint8_t *lb = lds + sb_slot * seg_cap + (sb_slot == 0 ? mis0 : mis1);
+        T res[PX * C];
+#pragma unroll
+        for (int p = 0; p < PX; ++p) {
+            if constexpr (NEAREST) {
+                T v[C];
+                __builtin_memcpy(v, la + toff[p], PB);
+#pragma unroll
+                for (int c = 0; c < C; ++c) res[p * C + c] = v[c];
+            } else {
+                // both taps of a row in one read: tap a at [0, PB), tap b at
+                // [PB, 2 PB); uint8 taps come in one 4- or 8-byte word so the
+                // read issues as a single (unaligned) LDS access.
+                if constexpr (sizeof(T) == 1) {
+                    using Wd = typename std::conditional<2 * PB <= 4, uint32_t, uint64_t>::type;
+                    Wd wa, wb;
+                    __builtin_memcpy(&wa, la + toff[p], sizeof(Wd));
+                    __builtin_memcpy(&wb, lb + toff[p], sizeof(Wd));
+                    const int sh = tnext[p] ? 8 * C : 0;
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        const unsigned a0 = (unsigned)(wa >> (8 * c)) & 255u;
+                        const unsigned a1 = (unsigned)(wa >> (8 * c + sh)) & 255u;
+                        const unsigned b0 = (unsigned)(wb >> (8 * c)) & 255u;
+                        const unsigned b1 = (unsigned)(wb >> (8 * c + sh)) & 255u;
+                        res[p * C + c] = (T)blend_u8(a0, a1, b0, b1, tw[p], wy1);
+                    }
+                } else {
+                    T ra2[2 * C], rb2[2 * C];
+                    __builtin_memcpy(ra2, la + toff[p], 2 * PB);
+                    __builtin_memcpy(rb2, lb + toff[p], 2 * PB);
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        const T a0 = ra2[c], a1 = tnext[p] ? ra2[C + c] : ra2[c];
+                        const T b0 = rb2[c], b1 = tnext[p] ? rb2[C + c] : rb2[c];
+                        res[p * C + c] = blend_f32(a0, a1, b0, b1, twf[p], wyf);
+                    }
+                }
+            }
+        }
+        if (valid_px > 0)
+            store_chunk<T, PX * C>(dst + ((size_t)g * dW + x0) * C, res, valid_px * C);
+        __syncthreads();
+        if (++dy == dH) {
+            dy = 0;
+            ++n;
+            ys.init(0, H, dH);
+        } else {
+            ys.next();
+        }
     }
 }
 

@@ -42,7 +42,8 @@
  * the device can access, e.g. torch CUDA tensors) owned by the caller.  The
  * library allocates nothing, keeps no state between calls and never takes
  * ownership.  The two byte ranges must not overlap.  Any alignment is
- * accepted; 16-byte aligned buffers take the vectorised paths.
+ * accepted for uint8; float32 buffers must be 4-byte aligned (element
+ * aligned).  16-byte aligned buffers take the vectorised paths.
  *
  * Stream: the work is enqueued on `stream` (a hipStream_t; NULL means the
  * null stream) and the call returns without waiting.  The caller synchronises
@@ -80,7 +81,8 @@ enum mi_resize_status {
     MI_RESIZE_ERR_CHANNELS = 3,  /* C is not 1, 3 or 4                        */
     MI_RESIZE_ERR_DTYPE = 4,     /* dtype is not MI_RESIZE_U8 / MI_RESIZE_F32 */
     MI_RESIZE_ERR_OVERLAP = 5,   /* src and dst byte ranges overlap           */
-    MI_RESIZE_ERR_HIP = 6        /* the HIP runtime refused the launch        */
+    MI_RESIZE_ERR_HIP = 6,       /* the HIP runtime refused the launch        */
+    MI_RESIZE_ERR_ALIGN = 7      /* float32 src or dst not 4-byte aligned     */
 };
 
 /* Linear (bilinear) resize; see the header comment for the exact result. */

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert R.resize_abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         s = R.resize_status_string(code)
         assert isinstance(s, str) and s
     assert R.resize_status_string(99) == "unknown status"
@@ -65,6 +65,9 @@ def test_argument_validation(name):
     assert call(name, src=FAKE_SRC, dst=FAKE_SRC + 5) == 5
     assert call(name, src=FAKE_SRC + 5, dst=FAKE_SRC) == 5
     assert call(name, src=FAKE_SRC, dst=FAKE_SRC + 8 * 8 * 3 - 1) == 5
+    # float32 buffers must be element aligned
+    assert call(name, dtype=1, src=FAKE_SRC + 2) == 7
+    assert call(name, dtype=1, dst=FAKE_DST + 1) == 7
     # checks come in a fixed order: null before dtype before channels before shape
     assert call(name, src=None, C=7, dtype=9) == 1
     assert call(name, C=7, dtype=9) == 4

@@ -82,13 +82,18 @@ def test_workload_full_size(name, mode):
                   "%s/%s" % (name, mode))
 
 
-@pytest.mark.parametrize("name", ["small", "4k", "up2x"])
-def test_workload_generic_kernel(name, monkeypatch):
+PATHS = ["rowseg", "direct"]   # MI_RESIZE_PATH: force one kernel family
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("name,mode", CASES)
+def test_workload_forced_path(name, mode, path, monkeypatch):
     w = WORKLOADS[name]
-    monkeypatch.setenv("MI_RESIZE_FORCE_GENERIC", "1")
-    say("case workload=%s generic kernel" % name)
+    monkeypatch.setenv("MI_RESIZE_PATH", path)
+    say("case workload=%s mode=%s path=%s" % (name, mode, path))
     s = make_source(w)
-    assert_parity(run_gpu(s, w.dH, w.dW), run_oracle(s, w.dH, w.dW), name + "/generic")
+    assert_parity(run_gpu(s, w.dH, w.dW, mode), run_oracle(s, w.dH, w.dW, mode),
+                  "%s/%s/%s" % (name, mode, path))
 
 
 # --------------------------------------------------------------------------
@@ -104,13 +109,16 @@ def random_case(r):
     return N, H, W, C, dH, dW
 
 
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
 @pytest.mark.parametrize("mode", ["linear", "nearest"])
-def test_random_shapes(dtype, mode):
-    r = np.random.default_rng(2024 + (dtype == "f32") + 2 * (mode == "nearest"))
+def test_random_shapes(dtype, mode, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
+    r = np.random.default_rng(2024 + (dtype == "f32") + 2 * (mode == "nearest") + 4 * (["auto"] + PATHS).index(path))
     for i in range(60):
         N, H, W, C, dH, dW = random_case(r)
-        say("case random %s %s #%d N=%d H=%d W=%d C=%d -> %dx%d" % (dtype, mode, i, N, H, W, C, dH, dW))
+        say("case random %s %s %s #%d N=%d H=%d W=%d C=%d -> %dx%d" % (dtype, mode, path, i, N, H, W, C, dH, dW))
         s = random_image(r, (N, H, W, C), dtype)
         assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
                       "random #%d %s" % (i, (N, H, W, C, dH, dW)))
@@ -131,6 +139,22 @@ def test_half_downscale_shapes(C):
 
 
 # --------------------------------------------------------------------------
+# exact 2x upscale (its own kernel): channel counts, batches, one-row and
+# one-chunk images, and widths that fall back to the generic kernels
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("C", [1, 3, 4])
+def test_double_upscale_shapes(C):
+    r = np.random.default_rng(91 + C)
+    for (N, H, W) in ((1, 1, 16), (2, 3, 32), (3, 17, 48), (1, 64, 1920), (1, 2, 8), (1, 1, 1),
+                      (2, 5, 24), (1, 9, 17), (4, 1, 160)):
+        s = random_image(r, (N, H, W, C), "u8")
+        for mode in ("linear", "nearest"):
+            say("case up2 %s C=%d N=%d src=%dx%d" % (mode, C, N, H, W))
+            assert_parity(run_gpu(s, 2 * H, 2 * W, mode), run_oracle(s, 2 * H, 2 * W, mode),
+                          "up2 %s %s" % (mode, (C, N, H, W)))
+
+
+# --------------------------------------------------------------------------
 # degenerate and extreme shapes
 # --------------------------------------------------------------------------
 EDGE = [
@@ -139,15 +163,20 @@ EDGE = [
     (1, 2, 65535, 1, 3, 40000), (1, 40000, 2, 1, 65535, 3), (1, 1, 65535, 4, 1, 65535),
     (4, 13, 17, 3, 13, 17), (1, 8, 8, 3, 8, 16), (1, 8, 8, 3, 16, 8),
     (7, 31, 33, 3, 61, 67), (1, 1000, 10, 1, 3, 999),
+    (1, 4, 4000, 3, 2, 37), (1, 3, 5000, 4, 3, 7), (2, 9, 1025, 1, 5, 1023), (1, 5, 1024, 1, 7, 1025),
+    (1, 6, 257, 3, 4, 255), (3, 17, 129, 4, 9, 131),
 ]
 
 
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
 @pytest.mark.parametrize("mode", ["linear", "nearest"])
-def test_edge_shapes(dtype, mode):
+def test_edge_shapes(dtype, mode, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
     r = np.random.default_rng(99)
     for (N, H, W, C, dH, dW) in EDGE:
-        say("case edge %s %s %s" % (dtype, mode, (N, H, W, C, dH, dW)))
+        say("case edge %s %s %s %s" % (dtype, mode, path, (N, H, W, C, dH, dW)))
         s = random_image(r, (N, H, W, C), dtype)
         assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
                       "edge %s" % ((N, H, W, C, dH, dW),))
@@ -163,9 +192,12 @@ def test_batch_of_tiny_images():
 # --------------------------------------------------------------------------
 # misaligned buffers take the scalar paths; results must not change
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
 @pytest.mark.parametrize("mode", ["linear", "nearest"])
-def test_misaligned_buffers(dtype, mode):
+def test_misaligned_buffers(dtype, mode, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
     r = np.random.default_rng(11)
     es = 1 if dtype == "u8" else 4
     for (N, H, W, C, dH, dW) in ((1, 64, 64, 4, 32, 32), (2, 40, 64, 3, 20, 32), (1, 33, 47, 1, 70, 20)):
@@ -188,8 +220,11 @@ def test_misaligned_buffers(dtype, mode):
 # --------------------------------------------------------------------------
 # nothing is written outside dst: canary bytes on both sides
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
-def test_guard_bands(dtype):
+def test_guard_bands(dtype, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
     r = np.random.default_rng(12)
     tdt = torch.uint8 if dtype == "u8" else torch.float32
     pad = 4096
