@@ -1,0 +1,45 @@
+"""Stored hand cases: the oracle reproduces them and each satisfies a closed
+form computed here (the cases come from tests/golden/make_golden.py)."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
+CASES = json.load(open(GOLDEN))["cases"]
+
+
+def arr(c):
+    return np.array(c["src"], dtype=np.uint8)[None, :, :, None]
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c["name"] for c in CASES])
+def test_oracle_reproduces(c):
+    dH, dW = c["dst_hw"]
+    f = oracle.resize_linear if c["mode"] == "linear" else oracle.resize_nearest
+    assert f(arr(c), dH, dW)[0, :, :, 0].tolist() == c["expected"]
+
+
+def by_name(n):
+    return next(c for c in CASES if c["name"] == n)
+
+
+def test_closed_forms():
+    s = np.array(by_name("ramp4_to_2x2")["src"], dtype=np.int64)
+    means = (s.reshape(2, 2, 2, 2).sum(axis=(1, 3)) + 2) // 4
+    assert by_name("ramp4_to_2x2")["expected"] == means.tolist()
+    # ramp value 16 (4y + x) at the clamped half-pixel coordinate, rounded half up
+    for name, n_out in (("ramp4_to_8x8", 8),):
+        exp = by_name(name)["expected"]
+        for dy in range(n_out):
+            y = min(max((Fraction(dy) + Fraction(1, 2)) * Fraction(4, n_out) - Fraction(1, 2), 0), 3)
+            for dx in range(n_out):
+                x = min(max((Fraction(dx) + Fraction(1, 2)) * Fraction(4, n_out) - Fraction(1, 2), 0), 3)
+                assert exp[dy][dx] == int(np.floor(16 * (4 * y + x) + Fraction(1, 2)))
+    assert by_name("ramp4_nearest_2x2")["expected"] == s[1::2, 1::2].tolist()
+    assert by_name("ramp4_nearest_8x8")["expected"] == s.repeat(2, 0).repeat(2, 1).tolist()
+    assert by_name("tie_2x2_to_1")["expected"] == [[1]]

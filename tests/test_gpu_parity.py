@@ -182,6 +182,17 @@ def test_edge_shapes(dtype, mode, path, monkeypatch):
                       "edge %s" % ((N, H, W, C, dH, dW),))
 
 
+def test_golden_hand_cases():
+    import json
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
+    for c in json.load(open(path))["cases"]:
+        say("case golden %s" % c["name"])
+        s = np.array(c["src"], dtype=np.uint8)[None, :, :, None]
+        dH, dW = c["dst_hw"]
+        got = run_gpu(s, dH, dW, c["mode"])[0, :, :, 0]
+        assert got.tolist() == c["expected"], c["name"]
+
+
 def test_batch_of_tiny_images():
     r = np.random.default_rng(5)
     s = random_image(r, (1000, 3, 2, 3), "u8")
