@@ -32,10 +32,21 @@ HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
 INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
-# dispatch, summed over the 8 XCDs), each scaled by the factor a plain copy of
-# known size reads on the same counter.  None until taken for the current
-# kernel; profiles/ holds the runs these come from.
-MEASURED_TRAFFIC = {}
+# dispatch), each scaled by the factor the same counter reads for the plain
+# 16-byte copy of 32 MiB (`bench.py --copy-calibration 33554432`: FETCH_SIZE
+# 16394.25 KiB -> x 1.9987, WRITE_SIZE 32768 KiB -> x 1.0).  Valid only for
+# the kernel named; profiles/linear_half_u8_4k_rgb_pmc_traffic.md holds the
+# runs.  Workloads without an entry report null.
+MEASURED_TRAFFIC = {
+    ("4k", "linear"): {"kernel": "linear_half_u8<3>", "fetch_kib": 12169.20, "write_kib": 6075.0,
+                       "fetch_scale": 1.9987, "write_scale": 1.0},
+}
+
+
+def traffic_bytes(entry):
+    if not entry:
+        return None
+    return round((entry["fetch_kib"] * entry["fetch_scale"] + entry["write_kib"] * entry["write_scale"]) * 1024)
 
 
 def parse():
@@ -208,7 +219,7 @@ def main():
         if not ok:
             sys.exit("bench output disagrees with the oracle")
 
-    traffic = MEASURED_TRAFFIC.get((w.name, mode))
+    traffic = traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode)))
     line = {
         "metric": "bilinear resize Gpix/s + HBM GB/s (% of peak), RGB u8 4K->1080p, 1 GPU",
         "value": round(gpix, 3),

@@ -105,13 +105,21 @@ constexpr long long kMaxGridY = 65535;
 template <int C>
 int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStream_t st)
 {
-    const int chunks_per_row = dW / HalfShape<C>::PX;
+    constexpr int seg = kHalfLanes * HalfShape<C>::PX;
     const long long rows = (long long)batch * dH;
-    const dim3 grid((chunks_per_row + kHalfBlock - 1) / kHalfBlock,
-                    (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
-    hipLaunchKernelGGL((linear_half_u8<C>), grid, dim3(kHalfBlock), 0, st, (const uint8_t *)src,
-                       (uint8_t *)dst, dW, rows, chunks_per_row);
+    const dim3 grid((dW + seg - 1) / seg, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
+    hipLaunchKernelGGL((linear_half_u8<C>), grid, dim3(kHalfLanes), 0, st, (const uint8_t *)src,
+                       (uint8_t *)dst, dW, rows);
     return launched();
+}
+
+// Exact 2:1 uint8 downscale whose rows split into whole 16-byte chunks and
+// whole lanes.
+bool half_path_fits(int C, int H, int W, int dH, int dW, const void *src, const void *dst)
+{
+    if (H != 2 * dH || W != 2 * dW || !aligned(src, 16) || !aligned(dst, 16)) return false;
+    const int q = C == 1 ? 16 : (C == 3 ? 8 : 4);
+    return dW % q == 0;
 }
 
 // LDS bytes one row-segment workgroup may use (two slots).  Beyond it the
@@ -188,13 +196,6 @@ bool up2_path_fits(int C, int H, int W, int dH, int dW, const void *src, const v
     return W % S == 0 && ((long long)W * C) % 16 == 0;
 }
 
-// Exact 2:1 uint8 downscale whose rows split into whole lanes.
-bool half_path_fits(int C, int H, int W, int dH, int dW, const void *src, const void *dst)
-{
-    if (H != 2 * dH || W != 2 * dW || !aligned(src, 16) || !aligned(dst, 16)) return false;
-    const int px = C == 1 ? HalfShape<1>::PX : C == 3 ? HalfShape<3>::PX : HalfShape<4>::PX;
-    return dW % px == 0;
-}
 
 template <int BPP>
 int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, int dW,

@@ -195,62 +195,99 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // general formula reduces, bit for bit, to the rounded 2x2 mean
 // (a + b + c + d + 2) >> 2.  No tap is ever clamped.
 //
-// A lane owns PX consecutive output pixels of one row: it loads 2 PX C bytes
-// from each of the two source rows and stores PX C bytes, with PX chosen so
-// that a lane moves 32-48 source bytes (C = 1: 8 px, 16 B per row; C = 3:
-// 4 px, 24 B per row; C = 4: 2 px, 16 B per row).  Measured on the 4K RGB
-// frame, lanes this small beat 8- and 16-pixel lanes: more lanes in flight
-// hide more HBM latency, and a lane's loads of both rows go out together.
-// Grid: x = 64-lane workgroups across a row, y = output rows (stride
-// gridDim.y).  Needs dW % PX == 0 and 16-byte aligned src / dst; then every
-// lane's accesses are naturally aligned.  Output row g reads source rows 2g
-// and 2g + 1 of the flattened N*H rows, because H = 2 dH.
+// A workgroup is one wave and owns a segment of 64 * PX output pixels of one
+// output row (PX = 16 for C = 1, 4 for C = 3 and 4).  Each source row of the
+// segment (2 PX C bytes per lane) is read with 16-byte non-temporal loads at
+// lane-consecutive addresses - every load instruction covers whole cache
+// lines, which is what lets the streaming hint help - and staged in LDS; each
+// lane then reads its 2 PX C bytes of both rows back, forms PX C means and
+// writes them with one contiguous store.  Measured on the 4K RGB frame this
+// beats lanes that load their own (strided) bytes directly by about 8 %, and
+// matches a plain kernel with the same 4:1 read / write byte mix.
+// Needs dW % (C == 1 ? 16 : C == 3 ? 8 : 4) == 0 and 16-byte aligned src /
+// dst, so every row and every 16-byte chunk is aligned.  Grid: x = segments
+// of a row, y = output rows (stride gridDim.y).  Output row g reads source
+// rows 2g and 2g + 1 of the flattened N * H rows, because H = 2 dH.
 // --------------------------------------------------------------------------
-template <int C> struct HalfShape;
-template <> struct HalfShape<1> { static constexpr int PX = 8; using LV = uint4; using SV = uint2; };
-template <> struct HalfShape<3> { static constexpr int PX = 4; using LV = uint2; using SV = uint32_t; };
-template <> struct HalfShape<4> { static constexpr int PX = 2; using LV = uint4; using SV = uint2; };
+template <int C> struct HalfShape { static constexpr int PX = C == 1 ? 16 : 4; };
 
-constexpr int kHalfBlock = 64;
+constexpr int kHalfLanes = 64;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint8_t *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int C>
-__global__ __launch_bounds__(kHalfBlock) void linear_half_u8(
-    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows,
-    int chunks_per_row)
+__global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows)
 {
-    using S = HalfShape<C>;
-    using LV = typename S::LV;
-    using SV = typename S::SV;
-    constexpr int INB = 2 * S::PX * C;            // source bytes per row per lane
-    constexpr int NIN = INB / (int)sizeof(LV);
-    constexpr int NOUT = S::PX * C;               // output bytes per lane
-    constexpr int NST = NOUT / (int)sizeof(SV);
-    const int j = blockIdx.x * kHalfBlock + threadIdx.x;
-    if (j >= chunks_per_row) return;
+    constexpr int PX = HalfShape<C>::PX;
+    constexpr int SEG = kHalfLanes * PX;          // output pixels per segment
+    constexpr int SRC_B = 2 * SEG * C;            // source bytes per row per segment
+    constexpr int NL = (SRC_B / 16 + kHalfLanes - 1) / kHalfLanes;   // loads per lane per row
+    constexpr int LB = 2 * PX * C;                // source bytes per lane per row
+    constexpr int OB = PX * C;                    // output bytes per lane
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SRC_B];
+
+    const int lane = threadIdx.x;
+    const int seg = blockIdx.x;
+    const int seg_px = min(SEG, dW - seg * SEG);
+    const int n16 = seg_px * 2 * C / 16;          // whole: dW meets the divisibility rule
     const size_t src_row = (size_t)2 * dW * C;
     const size_t dst_row = (size_t)dW * C;
     for (long long g = blockIdx.y; g < rows; g += gridDim.y) {
-        const LV *s0 = (const LV *)(src + (size_t)(2 * g) * src_row + (size_t)j * INB);
-        const LV *s1 = (const LV *)((const uint8_t *)s0 + src_row);
-        LV a[NIN], b[NIN];
+        const uint8_t *s0 = src + (size_t)(2 * g) * src_row + (size_t)seg * SRC_B;
+        const uint8_t *s1 = s0 + src_row;
+        uint4 va[NL], vb[NL];
 #pragma unroll
-        for (int k = 0; k < NIN; ++k) {
-            a[k] = s0[k];
-            b[k] = s1[k];
+        for (int i = 0; i < NL; ++i) {
+            const int k = lane + kHalfLanes * i;
+            if (k < n16) {
+                va[i] = load_stream(s0 + 16 * k);
+                vb[i] = load_stream(s1 + 16 * k);
+            }
         }
-        const uint8_t *pa = (const uint8_t *)a;
-        const uint8_t *pb = (const uint8_t *)b;
-        SV r[NST];
-        uint8_t *pr = (uint8_t *)r;
 #pragma unroll
-        for (int k = 0; k < NOUT; ++k) {
-            const int p = 2 * k - k % C;          // first source byte of output byte k
-            const unsigned s = (unsigned)pa[p] + pa[p + C] + pb[p] + pb[p + C] + 2u;
-            pr[k] = (uint8_t)(s >> 2);
+        for (int i = 0; i < NL; ++i) {
+            const int k = lane + kHalfLanes * i;
+            if (k < n16) {
+                *(uint4 *)(lds + 16 * k) = va[i];
+                *(uint4 *)(lds + SRC_B + 16 * k) = vb[i];
+            }
         }
-        SV *o = (SV *)(dst + (size_t)g * dst_row + (size_t)j * NOUT);
+        __syncthreads();
+        if (lane * PX < seg_px) {
+            uint8_t a[LB], b[LB];
+            __builtin_memcpy(a, lds + LB * lane, LB);
+            __builtin_memcpy(b, lds + SRC_B + LB * lane, LB);
+            uint8_t r[OB];
 #pragma unroll
-        for (int k = 0; k < NST; ++k) o[k] = r[k];
+            for (int k = 0; k < OB; ++k) {
+                const int p = 2 * k - k % C;      // first source byte of output byte k
+                r[k] = (uint8_t)(((unsigned)a[p] + a[p + C] + b[p] + b[p + C] + 2u) >> 2);
+            }
+            uint8_t *o = dst + (size_t)g * dst_row + (size_t)seg * SEG * C + (size_t)lane * OB;
+            if constexpr (OB % 16 == 0) {
+#pragma unroll
+                for (int k = 0; k < OB / 16; ++k) {
+                    uint4 q;
+                    __builtin_memcpy(&q, r + 16 * k, 16);
+                    ((uint4 *)o)[k] = q;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < OB / 4; ++k) {
+                    uint32_t q;
+                    __builtin_memcpy(&q, r + 4 * k, 4);
+                    ((uint32_t *)o)[k] = q;
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
