@@ -124,7 +124,8 @@ bool half_path_fits(int C, int H, int W, int dH, int dW, const void *src, const 
 
 // LDS bytes one row-segment workgroup may use (two slots).  Beyond it the
 // segment is too wide (strong downscale) and the direct kernels run instead;
-// at 16 KiB a CU still holds 10 such one-wave workgroups.
+// at 16 KiB a CU still holds 10 such one-wave workgroups, and a slot of at
+// most 8 KiB is at most 8 16-byte chunks per lane.
 constexpr int kSegLdsBudget = 16 * 1024;
 // One-wave workgroups a row-segment launch aims for: 32 per CU on 256 CUs.
 constexpr long long kSegTargetBlocks = 8192;
@@ -166,9 +167,17 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const long long rows = (long long)batch * dH;
     SegPlan pl;
     if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, pl)) return false;
-    hipLaunchKernelGGL((rowseg<T, C, NEAREST>), pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st,
-                       (const T *)src, (T *)dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
-                       (long long)batch * H * W * C);
+    // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8
+    const int per_lane = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src,
+                           (T *)dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
+                           (long long)batch * H * W * C);
+    };
+    if (per_lane <= 1) go(rowseg<T, C, NEAREST, 1>);
+    else if (per_lane <= 2) go(rowseg<T, C, NEAREST, 2>);
+    else if (per_lane <= 4) go(rowseg<T, C, NEAREST, 4>);
+    else go(rowseg<T, C, NEAREST, 8>);
     rc = launched();
     return true;
 }

@@ -493,36 +493,75 @@ template <> struct SegShape<uint8_t, 3> { static constexpr int PX = 4; };
 template <> struct SegShape<uint8_t, 4> { static constexpr int PX = 4; };
 template <> struct SegShape<float, 1> { static constexpr int PX = 4; };
 template <> struct SegShape<float, 3> { static constexpr int PX = 4; };
-template <> struct SegShape<float, 4> { static constexpr int PX = 2; };
+template <> struct SegShape<float, 4> { static constexpr int PX = 1; };
 
 constexpr int kSegLanes = 64;
 constexpr int kSegReadSlack = 16;  // bytes a two-tap LDS read may run past the segment
 
-// Stage `bytes` bytes of the source starting at p0 into an LDS slot, as
-// 16-byte chunks from the 16-byte boundary at or below p0, one chunk per
-// lane per step.  Chunks that are not wholly inside [lo, hi) are copied
-// byte by byte, so nothing outside the source buffer is read.  Returns p0's
-// offset from that boundary (its position in the slot).
-__device__ __forceinline__ int stage_segment(uint8_t *slot, const uint8_t *p0, int bytes,
-                                             const uint8_t *lo, const uint8_t *hi)
-{
-    const int m = (int)((uintptr_t)p0 & 15);
-    const uint8_t *a0 = p0 - m;
-    const int n16 = (m + bytes + 15) >> 4;
-    for (int k = threadIdx.x; k < n16; k += kSegLanes) {
-        const uint8_t *q = a0 + 16 * k;
-        uint4 v;
-        if (q >= lo && q + 16 <= hi) {
-            v = *(const uint4 *)q;
-        } else {
-            uint8_t t[16];
+// One source-row segment to stage: `bytes` bytes from p (uniform across the
+// wave) into an LDS slot, as 16-byte chunks from the 16-byte boundary at or
+// below p.  Chunks [k_lo, k_hi) lie wholly inside the source buffer and are
+// loaded as one 16-byte access each; the rest (only at the very start or end
+// of the buffer) are copied byte by byte, so nothing outside is read.
+struct Segment {
+    const uint8_t *base;   // 16-byte aligned address of chunk 0
+    uint8_t *slot;
+    int mis;               // offset of p inside the slot
+    int n16, k_lo, k_hi;
+    bool on;
+    __device__ void plan(bool want, uint8_t *slot_, const uint8_t *p, int bytes,
+                         const uint8_t *lo, const uint8_t *hi)
+    {
+        on = want;
+        slot = slot_;
+        mis = (int)((uintptr_t)p & 15);
+        base = p - mis;
+        n16 = (mis + bytes + 15) >> 4;
+        const long long first = base >= lo ? 0 : (long long)((lo - base + 15) >> 4);
+        const long long last = (long long)((hi - base) >> 4);   // chunks [0, last) end at or before hi
+        k_lo = (int)(first < n16 ? first : n16);
+        k_hi = (int)(last < n16 ? (last > k_lo ? last : k_lo) : n16);
+    }
+    __device__ void write_edge(int k, const uint8_t *lo, const uint8_t *hi) const
+    {
+        const uint8_t *q = base + 16 * k;
+        uint8_t t[16];
 #pragma unroll
-            for (int b = 0; b < 16; ++b) t[b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
-            __builtin_memcpy(&v, t, 16);
-        }
+        for (int b = 0; b < 16; ++b) t[b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
+        uint4 v;
+        __builtin_memcpy(&v, t, 16);
         *(uint4 *)(slot + 16 * k) = v;
     }
-    return m;
+};
+
+// Stage up to two segments with every global load of the lane issued before
+// any LDS write, so the wave waits for memory once per output row, not once
+// per chunk.  KMAX bounds the chunks per lane per segment (n16 <= 64 KMAX).
+template <int KMAX>
+__device__ __forceinline__ void stage_pair(const Segment &A, const Segment &B,
+                                           const uint8_t *lo, const uint8_t *hi)
+{
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x;
+    v4u va[KMAX], vb[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const int k = lane + kSegLanes * i;
+        va[i] = (A.on && k >= A.k_lo && k < A.k_hi) ? *(const v4u *)(A.base + 16 * k) : v4u{0, 0, 0, 0};
+        vb[i] = (B.on && k >= B.k_lo && k < B.k_hi) ? *(const v4u *)(B.base + 16 * k) : v4u{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const int k = lane + kSegLanes * i;
+        if (A.on && k < A.n16) {
+            if (k >= A.k_lo && k < A.k_hi) *(v4u *)(A.slot + 16 * k) = va[i];
+            else A.write_edge(k, lo, hi);
+        }
+        if (B.on && k < B.n16) {
+            if (k >= B.k_lo && k < B.k_hi) *(v4u *)(B.slot + 16 * k) = vb[i];
+            else B.write_edge(k, lo, hi);
+        }
+    }
 }
 
 // Store N elements of one lane: vectorised when the chunk is whole and
@@ -575,7 +614,7 @@ struct RowStepper {
     }
 };
 
-template <typename T, int C, bool NEAREST>
+template <typename T, int C, bool NEAREST, int KMAX>
 __global__ __launch_bounds__(kSegLanes) void rowseg(
     const T *__restrict__ src, T *__restrict__ dst, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int seg_cap, long long src_elems)
@@ -625,6 +664,7 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
     const uint8_t *lo = (const uint8_t *)src;
     const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
     const size_t row_bytes = (size_t)W * PB;
+    T *const out_lane = dst + (size_t)x0 * C;
 
     long long g = (long long)blockIdx.y * rows_per_block;
     long long g_end = g + rows_per_block;
@@ -658,21 +698,22 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
         const long long ra = n * H + ya, rb = n * H + yb;
         int sa_slot = held0 == ra ? 0 : (held1 == ra ? 1 : -1);
         int sb_slot = held0 == rb ? 0 : (held1 == rb ? 1 : -1);
-        if (sa_slot < 0) {
-            sa_slot = (sb_slot == 0) ? 1 : 0;
-            const int m = stage_segment(lds + sa_slot * seg_cap,
-                                        lo + (size_t)ra * row_bytes + (size_t)sa * PB,
-                                        seg_bytes, lo, hi);
-            if (sa_slot == 0) { held0 = ra; mis0 = m; } else { held1 = ra; mis1 = m; }
+        const bool need_a = sa_slot < 0;
+        if (need_a) sa_slot = (sb_slot == 0) ? 1 : 0;
+        if (rb == ra) sb_slot = sa_slot;
+        const bool need_b = sb_slot < 0;
+        if (need_b) sb_slot = 1 - sa_slot;
+        Segment A, B;
+        A.plan(need_a, lds + sa_slot * seg_cap, lo + (size_t)ra * row_bytes + (size_t)sa * PB,
+               seg_bytes, lo, hi);
+        B.plan(need_b, lds + sb_slot * seg_cap, lo + (size_t)rb * row_bytes + (size_t)sa * PB,
+               seg_bytes, lo, hi);
+        stage_pair<KMAX>(A, B, lo, hi);
+        if (need_a) {
+            if (sa_slot == 0) { held0 = ra; mis0 = A.mis; } else { held1 = ra; mis1 = A.mis; }
         }
-        if (rb == ra) {
-            sb_slot = sa_slot;
-        } else if (sb_slot < 0) {
-            sb_slot = 1 - sa_slot;
-            const int m = stage_segment(lds + sb_slot * seg_cap,
-                                        lo + (size_t)rb * row_bytes + (size_t)sa * PB,
-                                        seg_bytes, lo, hi);
-            if (sb_slot == 0) { held0 = rb; mis0 = m; } else { held1 = rb; mis1 = m; }
+        if (need_b) {
+            if (sb_slot == 0) { held0 = rb; mis0 = B.mis; } else { held1 = rb; mis1 = B.mis; }
         }
         __syncthreads();
 
@@ -691,18 +732,35 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
                 // [PB, 2 PB); uint8 taps come in one 4- or 8-byte word so the
                 // read issues as a single (unaligned) LDS access.
                 if constexpr (sizeof(T) == 1) {
-                    using Wd = typename std::conditional<2 * PB <= 4, uint32_t, uint64_t>::type;
-                    Wd wa, wb;
-                    __builtin_memcpy(&wa, la + toff[p], sizeof(Wd));
-                    __builtin_memcpy(&wb, lb + toff[p], sizeof(Wd));
-                    const int sh = tnext[p] ? 8 * C : 0;
+                    // tap a = bytes [0, C), tap b = bytes [C, 2C) of the word
+                    // (or tap a again where both taps clamp to one column)
+                    uint32_t a_lo, a_hi, b_lo, b_hi;
+                    if constexpr (2 * PB <= 4) {
+                        __builtin_memcpy(&a_lo, la + toff[p], 4);
+                        __builtin_memcpy(&b_lo, lb + toff[p], 4);
+                        a_hi = a_lo;
+                        b_hi = b_lo;
+                    } else {
+                        uint64_t wa, wb;
+                        __builtin_memcpy(&wa, la + toff[p], 8);
+                        __builtin_memcpy(&wb, lb + toff[p], 8);
+                        a_lo = (uint32_t)wa;
+                        a_hi = (uint32_t)(wa >> 32);
+                        b_lo = (uint32_t)wb;
+                        b_hi = (uint32_t)(wb >> 32);
+                    }
+                    // the second tap's C bytes, shifted down to byte 0
+                    const uint32_t a2 = tnext[p] ? __builtin_amdgcn_alignbyte(a_hi, a_lo, C % 4 == 0 ? 0 : C)
+                                                 : a_lo;
+                    const uint32_t b2 = tnext[p] ? __builtin_amdgcn_alignbyte(b_hi, b_lo, C % 4 == 0 ? 0 : C)
+                                                 : b_lo;
+                    const uint32_t a2w = (C == 4 && tnext[p]) ? a_hi : a2;
+                    const uint32_t b2w = (C == 4 && tnext[p]) ? b_hi : b2;
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
-                        const unsigned a0 = (unsigned)(wa >> (8 * c)) & 255u;
-                        const unsigned a1 = (unsigned)(wa >> (8 * c + sh)) & 255u;
-                        const unsigned b0 = (unsigned)(wb >> (8 * c)) & 255u;
-                        const unsigned b1 = (unsigned)(wb >> (8 * c + sh)) & 255u;
-                        res[p * C + c] = (T)blend_u8(a0, a1, b0, b1, tw[p], wy1);
+                        const unsigned p00 = (a_lo >> (8 * c)) & 255u, p01 = (a2w >> (8 * c)) & 255u;
+                        const unsigned p10 = (b_lo >> (8 * c)) & 255u, p11 = (b2w >> (8 * c)) & 255u;
+                        res[p * C + c] = (T)blend_u8(p00, p01, p10, p11, tw[p], wy1);
                     }
                 } else {
                     T ra2[2 * C], rb2[2 * C];
@@ -718,7 +776,7 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
             }
         }
         if (valid_px > 0)
-            store_chunk<T, PX * C>(dst + ((size_t)g * dW + x0) * C, res, valid_px * C);
+            store_chunk<T, PX * C>(out_lane + (size_t)g * dW * C, res, valid_px * C);
         __syncthreads();
         if (++dy == dH) {
             dy = 0;
