@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="4k")
     p.add_argument("--mode", default=None, help="linear (default) or nearest")
+    p.add_argument("--op", default="resize", choices=["resize", "normalize"],
+                   help="normalize: the fused uint8 -> float32 NCHW resize + normalisation "
+                        "(ImageNet mean / std, alpha 1/255) on the same workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
@@ -163,11 +166,20 @@ def main():
 
     src_np = make_source(w)
     tdt = torch.uint8 if w.dtype == "u8" else torch.float32
-    pair_bytes = w.src_bytes + w.dst_bytes
-    pairs = 1 if args.warm else max(2, -(-2 * INFINITY_CACHE_BYTES // pair_bytes))
     src0 = torch.from_numpy(src_np).to(dev)
+    fused = args.op == "normalize"
+    if fused:
+        if w.dtype != "u8" or mode != "linear":
+            sys.exit("--op normalize needs a uint8 linear workload")
+        dst_shape = (w.batch, w.C, w.dH, w.dW)
+        dst_bytes = w.dst_pixels * w.C * 4
+        tdt_out = torch.float32
+    else:
+        dst_shape, dst_bytes, tdt_out = w.dst_shape, w.dst_bytes, tdt
+    pair_bytes = w.src_bytes + dst_bytes
+    pairs = 1 if args.warm else max(2, -(-2 * INFINITY_CACHE_BYTES // pair_bytes))
     srcs = [src0] + [src0.clone() for _ in range(pairs - 1)]
-    dsts = [torch.empty(w.dst_shape, dtype=tdt, device=dev) for _ in range(pairs)]
+    dsts = [torch.empty(dst_shape, dtype=tdt_out, device=dev) for _ in range(pairs)]
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize(dev)
 
@@ -176,6 +188,14 @@ def main():
     lib = R._load()
     entry = lib.resize_linear if mode == "linear" else lib.resize_nearest
     code = R.U8 if w.dtype == "u8" else R.F32
+    if fused:
+        import ctypes
+        fa = ctypes.c_float * 4
+        mean_c, std_c = fa(0.485, 0.456, 0.406, 0.5), fa(0.229, 0.224, 0.225, 0.25)
+        base = lib.resize_linear_normalize
+
+        def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
+            return base(s_, d_, N_, H_, W_, C_, dH_, dW_, 1.0 / 255.0, mean_c, std_c, 1, sh_)
     sh = stream.cuda_stream
     sp = [t.data_ptr() for t in srcs]
     dp = [t.data_ptr() for t in dsts]
@@ -242,13 +262,18 @@ def main():
     # correctness of what was timed: the last buffer written, vs the oracle
     if not args.no_cpu:
         import oracle
-        ref = (oracle.resize_linear if mode == "linear" else oracle.resize_nearest)(src_np, w.dH, w.dW)
         got = dsts[(K - 1) % pairs].cpu().numpy()
-        ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
+        if fused:
+            ref = oracle.resize_linear_normalize(src_np, w.dH, w.dW, 1 / 255, (0.485, 0.456, 0.406, 0.5)[:w.C],
+                                                 (0.229, 0.224, 0.225, 0.25)[:w.C], "NCHW")
+            ok = bool((np.abs(got - ref) <= 1e-5 * np.maximum(1.0, np.abs(ref))).all())
+        else:
+            ref = (oracle.resize_linear if mode == "linear" else oracle.resize_nearest)(src_np, w.dH, w.dW)
+            ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
         if not ok:
             sys.exit("bench output disagrees with the oracle")
 
-    traffic = traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode)))
+    traffic = None if fused else traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode)))
     line = {
         "metric": "bilinear resize Gpix/s + HBM GB/s (% of peak), RGB u8 4K->1080p, 1 GPU",
         "value": round(gpix, 3),
@@ -263,8 +288,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s" % (
-                w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode),
+            "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s%s" % (
+                w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode,
+                " + normalize to f32 NCHW" if fused else ""),
             "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
             "mode": mode, "cache": "warm (1 pair)" if args.warm else "cold (%d rotating pairs)" % pairs,
         },

@@ -23,7 +23,7 @@ import ctypes
 import os
 
 __all__ = [
-    "resize", "resize_linear", "resize_nearest", "resize_copy_bytes",
+    "resize", "resize_linear", "resize_nearest", "resize_linear_normalize", "resize_copy_bytes",
     "resize_status_string", "resize_abi_version", "library_path", "ResizeError",
     "U8", "F32",
 ]
@@ -33,7 +33,7 @@ _LIB_PATH = os.path.join(_PKG, "libmi_resize.so")
 
 U8 = 0
 F32 = 1
-_ABI_VERSION = 1
+_ABI_VERSION = 2
 
 _lib = None
 
@@ -70,6 +70,10 @@ def _load():
     lib.resize_abi_version.restype = ci
     lib.resize_copy_bytes.argtypes = [vp, vp, i64, vp]
     lib.resize_copy_bytes.restype = ci
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.resize_linear_normalize.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float,
+                                            fp, fp, ci, vp]
+    lib.resize_linear_normalize.restype = ci
     if lib.resize_abi_version() != _ABI_VERSION:
         raise RuntimeError("libmi_resize.so ABI version %d, binding expects %d"
                            % (lib.resize_abi_version(), _ABI_VERSION))
@@ -149,6 +153,46 @@ def resize_linear(src, dst, stream=None):
 def resize_nearest(src, dst, stream=None):
     """Nearest-neighbour resize of ``src`` into ``dst``; see resize_linear."""
     return _call("resize_nearest", src, dst, stream)
+
+
+LAYOUTS = {"NHWC": 0, "NCHW": 1}
+
+
+def resize_linear_normalize(src, dst, mean, std, alpha=1.0 / 255.0, layout="NCHW", stream=None):
+    """Linear resize of a uint8 HWC / NHWC tensor fused with normalisation
+    into a caller-owned float32 ``dst``:  dst = (v * alpha - mean[c]) / std[c],
+    v being exactly resize_linear's uint8 result.  ``layout`` "NCHW" (dst is
+    (N,) C x dst_H x dst_W) or "NHWC" (dst is (N,) dst_H x dst_W x C)."""
+    import torch
+    N, H, W, C = _nhwc(src, "src")
+    if src.dtype != torch.uint8:
+        raise TypeError("src must be uint8")
+    if not isinstance(dst, torch.Tensor) or dst.dtype != torch.float32:
+        raise TypeError("dst must be a float32 tensor")
+    if dst.device != src.device or not dst.is_contiguous():
+        raise ValueError("dst must be contiguous and on src's device")
+    if layout not in LAYOUTS:
+        raise ValueError("layout must be 'NCHW' or 'NHWC'")
+    shape = tuple(dst.shape) if dst.dim() == 4 else (1,) + tuple(dst.shape)
+    if dst.dim() != src.dim() or len(shape) != 4:
+        raise ValueError("dst must be batched exactly when src is")
+    if layout == "NHWC":
+        N2, dH, dW, C2 = shape
+    else:
+        N2, C2, dH, dW = shape
+    if (N2, C2) != (N, C):
+        raise ValueError("dst shape %s does not match src %s" % (tuple(dst.shape), tuple(src.shape)))
+    mean = [float(v) for v in mean]
+    std = [float(v) for v in std]
+    if len(mean) != C or len(std) != C:
+        raise ValueError("mean and std need one value per channel")
+    fa = ctypes.c_float * C
+    rc = _load().resize_linear_normalize(src.data_ptr(), dst.data_ptr(), N, H, W, C, dH, dW,
+                                         float(alpha), fa(*mean), fa(*std), LAYOUTS[layout],
+                                         _stream_handle(stream, src.device))
+    if rc != 0:
+        raise ResizeError(rc, "resize_linear_normalize")
+    return dst
 
 
 def resize(src, size=None, mode: str = "linear", scale=None, stream=None):

@@ -3,6 +3,7 @@
 #include "mi_resize.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -81,21 +82,22 @@ int launched()
     return hipGetLastError() == hipSuccess ? MI_RESIZE_OK : MI_RESIZE_ERR_HIP;
 }
 
-template <typename T, int C>
+template <typename T, int C, int OUT = kOutSame>
 int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                          hipStream_t st)
+                          hipStream_t st, const Affine &aff = Affine{})
 {
     const long long rows = (long long)batch * dH;
     const Grid g = band_grid(rows, dW);
-    const bool pix4 = C == 4 && aligned(src, 4 * sizeof(T)) && aligned(dst, 4 * sizeof(T));
+    const bool pix4 = OUT == kOutSame && C == 4 && aligned(src, 4 * sizeof(T)) &&
+                      aligned(dst, 4 * sizeof(T));
     if (pix4) {
-        hipLaunchKernelGGL((linear_generic<T, C, C == 4>), dim3(g.blocks), dim3(kBlock), 0, st,
-                           (const T *)src, (T *)dst, H, W, dH, dW, rows, g.rows_per_block,
-                           g.col_blocks);
+        hipLaunchKernelGGL((linear_generic<T, C, C == 4 && OUT == kOutSame, OUT>), dim3(g.blocks), dim3(kBlock), 0,
+                           st, (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block,
+                           g.col_blocks, aff);
     } else {
-        hipLaunchKernelGGL((linear_generic<T, C, false>), dim3(g.blocks), dim3(kBlock), 0, st,
-                           (const T *)src, (T *)dst, H, W, dH, dW, rows, g.rows_per_block,
-                           g.col_blocks);
+        hipLaunchKernelGGL((linear_generic<T, C, false, OUT>), dim3(g.blocks), dim3(kBlock), 0,
+                           st, (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block,
+                           g.col_blocks, aff);
     }
     return launched();
 }
@@ -160,9 +162,9 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, SegPlan
     return true;
 }
 
-template <typename T, int C, bool NEAREST>
+template <typename T, int C, bool NEAREST, int OUT = kOutSame>
 bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                hipStream_t st, int &rc)
+                hipStream_t st, int &rc, const Affine &aff = Affine{})
 {
     const long long rows = (long long)batch * dH;
     SegPlan pl;
@@ -171,13 +173,13 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const int per_lane = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src,
-                           (T *)dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
-                           (long long)batch * H * W * C);
+                           dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
+                           (long long)batch * H * W * C, aff);
     };
-    if (per_lane <= 1) go(rowseg<T, C, NEAREST, 1>);
-    else if (per_lane <= 2) go(rowseg<T, C, NEAREST, 2>);
-    else if (per_lane <= 4) go(rowseg<T, C, NEAREST, 4>);
-    else go(rowseg<T, C, NEAREST, 8>);
+    if (per_lane <= 1) go(rowseg<T, C, NEAREST, 1, OUT>);
+    else if (per_lane <= 2) go(rowseg<T, C, NEAREST, 2, OUT>);
+    else if (per_lane <= 4) go(rowseg<T, C, NEAREST, 4, OUT>);
+    else go(rowseg<T, C, NEAREST, 8, OUT>);
     rc = launched();
     return true;
 }
@@ -260,6 +262,19 @@ int nearest_dispatch(const void *src, void *dst, int batch, int H, int W, int dH
     return launch_nearest<BPP>(src, dst, batch, H, W, dH, dW, st);
 }
 
+template <int C, int OUT>
+int normalize_dispatch(const void *src, float *dst, int batch, int H, int W, int dH, int dW,
+                       hipStream_t st, const Affine &aff)
+{
+    const Path path = path_override();
+    int rc;
+    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    if (path == Path::RowSeg || (path == Path::Auto && !small))
+        if (try_rowseg<uint8_t, C, false, OUT>(src, dst, batch, H, W, dH, dW, st, rc, aff))
+            return rc;
+    return launch_linear_generic<uint8_t, C, OUT>(src, dst, batch, H, W, dH, dW, st, aff);
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +294,9 @@ const char *resize_status_string(int status)
     case MI_RESIZE_ERR_OVERLAP: return "src and dst buffers overlap";
     case MI_RESIZE_ERR_HIP: return "the HIP runtime refused the kernel launch";
     case MI_RESIZE_ERR_ALIGN: return "float32 src and dst must be 4-byte aligned";
+    case MI_RESIZE_ERR_PARAM:
+        return "bad normalisation parameters (mean/std must be non-null, std finite and "
+               "non-zero, alpha finite, layout 0 or 1)";
     default: return "unknown status";
     }
 }
@@ -320,6 +338,44 @@ int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C, i
     case 1: return nearest_dispatch<4, float, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
     case 3: return nearest_dispatch<12, float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
     default: return nearest_dispatch<16, float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+    }
+}
+
+int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W, int C,
+                            int dst_H, int dst_W, float alpha, const float *mean,
+                            const float *std_dev, int layout, void *stream)
+{
+    if (!src || !dst) return MI_RESIZE_ERR_NULL;
+    if (C != 1 && C != 3 && C != 4) return MI_RESIZE_ERR_CHANNELS;
+    if (batch < 1 || H < 1 || W < 1 || dst_H < 1 || dst_W < 1 || H > kMaxDim || W > kMaxDim ||
+        dst_H > kMaxDim || dst_W > kMaxDim || (long long)batch * dst_H * dst_W > kMaxOutPixels)
+        return MI_RESIZE_ERR_SHAPE;
+    if (!mean || !std_dev || (layout != 0 && layout != 1) || !isfinite(alpha))
+        return MI_RESIZE_ERR_PARAM;
+    Affine aff{};
+    for (int c = 0; c < C; ++c) {
+        const double sd = std_dev[c], mu = mean[c];
+        if (!isfinite(sd) || sd == 0.0 || !isfinite(mu)) return MI_RESIZE_ERR_PARAM;
+        aff.scale[c] = (float)((double)alpha / sd);
+        aff.bias[c] = (float)(-mu / sd);
+    }
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    const uintptr_t s1 = s0 + (size_t)batch * H * W * C;
+    const uintptr_t d1 = d0 + (size_t)batch * dst_H * dst_W * C * sizeof(float);
+    if (s0 < d1 && d0 < s1) return MI_RESIZE_ERR_OVERLAP;
+    if (!aligned(dst, 4)) return MI_RESIZE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (layout == 0) {
+        switch (C) {
+        case 1: return normalize_dispatch<1, kOutNormNHWC>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
+        case 3: return normalize_dispatch<3, kOutNormNHWC>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
+        default: return normalize_dispatch<4, kOutNormNHWC>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
+        }
+    }
+    switch (C) {
+    case 1: return normalize_dispatch<1, kOutNormNCHW>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
+    case 3: return normalize_dispatch<3, kOutNormNCHW>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
+    default: return normalize_dispatch<4, kOutNormNCHW>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
     }
 }
 

@@ -107,17 +107,34 @@ __device__ __forceinline__ float blend_f32(float p00, float p01, float p10, floa
 }
 
 // --------------------------------------------------------------------------
+// Output stage.  kOutSame stores the resized elements in the source type.
+// The normalising stages (uint8 sources) store float32
+//     out = v * scale[c] + bias[c]      (one fused multiply-add)
+// where v is the exact uint8 resize result, either interleaved like the
+// source (NHWC) or as one plane per channel (NCHW).  The host derives
+// scale = alpha / std and bias = -mean / std in double precision.
+// --------------------------------------------------------------------------
+enum : int { kOutSame = 0, kOutNormNHWC = 1, kOutNormNCHW = 2 };
+
+struct Affine {
+    float scale[4];
+    float bias[4];
+};
+
+// --------------------------------------------------------------------------
 // Generic linear resize, any scale, C in {1, 3, 4}.  Grid: 1-D,
 // blockIdx = row_block * col_blocks + col_block.  A block covers kBlock
 // output columns of `rows_per_block` consecutive global rows; one lane per
 // output pixel per row.  PIX4: C == 4 and the buffers are aligned so that a
 // whole pixel moves as one 4-byte (u8) or 16-byte (f32) access.
 // --------------------------------------------------------------------------
-template <typename T, int C, bool PIX4>
+template <typename T, int C, bool PIX4, int OUT = kOutSame>
 __global__ __launch_bounds__(kBlock) void linear_generic(
-    const T *__restrict__ src, T *__restrict__ dst, int H, int W, int dH, int dW,
-    long long rows_total, int rows_per_block, int col_blocks)
+    const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
+    long long rows_total, int rows_per_block, int col_blocks, Affine aff)
 {
+    T *const dst = (T *)dst_v;
+    float *const dstf = (float *)dst_v;
     const int cb = (int)(blockIdx.x % (unsigned)col_blocks);
     const long long rb = blockIdx.x / (unsigned)col_blocks;
     const int x = cb * kBlock + (int)threadIdx.x;
@@ -159,11 +176,22 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                                   (d >> s) & 255u, wx1, wy1) << s;
                 }
                 *(uint32_t *)out = o;
-            } else {
+            } else if constexpr (OUT == kOutSame) {
 #pragma unroll
                 for (int k = 0; k < C; ++k)
                     out[k] = (uint8_t)blend_u8(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k],
                                                wx1, wy1);
+            } else {
+#pragma unroll
+                for (int k = 0; k < C; ++k) {
+                    const float v = (float)blend_u8(r0[xa + k], r0[xb + k], r1[xa + k],
+                                                    r1[xb + k], wx1, wy1);
+                    const float o = fmaf(v, aff.scale[k], aff.bias[k]);
+                    if constexpr (OUT == kOutNormNHWC)
+                        dstf[((size_t)g * dW + x) * C + k] = o;
+                    else
+                        dstf[(((size_t)n * C + k) * dH + dy) * dW + x] = o;
+                }
             }
         } else {
             const float wyf = weightf(ty);
@@ -614,11 +642,12 @@ struct RowStepper {
     }
 };
 
-template <typename T, int C, bool NEAREST, int KMAX>
+template <typename T, int C, bool NEAREST, int KMAX, int OUT = kOutSame>
 __global__ __launch_bounds__(kSegLanes) void rowseg(
-    const T *__restrict__ src, T *__restrict__ dst, int H, int W, int dH, int dW,
-    long long rows_total, int rows_per_block, int seg_cap, long long src_elems)
+    const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
+    long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff)
 {
+    T *const dst = (T *)dst_v;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int PX = SegShape<T, C>::PX;
     constexpr int PB = C * (int)sizeof(T);        // bytes per pixel
@@ -775,8 +804,29 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
                 }
             }
         }
-        if (valid_px > 0)
-            store_chunk<T, PX * C>(out_lane + (size_t)g * dW * C, res, valid_px * C);
+        if (valid_px > 0) {
+            if constexpr (OUT == kOutSame) {
+                store_chunk<T, PX * C>(out_lane + (size_t)g * dW * C, res, valid_px * C);
+            } else {
+                float f[PX * C];
+#pragma unroll
+                for (int k = 0; k < PX * C; ++k)
+                    f[k] = fmaf((float)res[k], aff.scale[k % C], aff.bias[k % C]);
+                float *dstf = (float *)dst_v;
+                if constexpr (OUT == kOutNormNHWC) {
+                    store_chunk<float, PX * C>(dstf + ((size_t)g * dW + x0) * C, f, valid_px * C);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        float plane[PX];
+#pragma unroll
+                        for (int p = 0; p < PX; ++p) plane[p] = f[p * C + c];
+                        store_chunk<float, PX>(dstf + (((size_t)n * C + c) * dH + dy) * dW + x0,
+                                               plane, valid_px);
+                    }
+                }
+            }
+        }
         __syncthreads();
         if (++dy == dH) {
             dy = 0;

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MI_RESIZE_ABI_VERSION 1
+#define MI_RESIZE_ABI_VERSION 2
 
 enum mi_resize_dtype {
     MI_RESIZE_U8 = 0,   /* uint8_t elements  */
@@ -82,7 +82,8 @@ enum mi_resize_status {
     MI_RESIZE_ERR_DTYPE = 4,     /* dtype is not MI_RESIZE_U8 / MI_RESIZE_F32 */
     MI_RESIZE_ERR_OVERLAP = 5,   /* src and dst byte ranges overlap           */
     MI_RESIZE_ERR_HIP = 6,       /* the HIP runtime refused the launch        */
-    MI_RESIZE_ERR_ALIGN = 7      /* float32 src or dst not 4-byte aligned     */
+    MI_RESIZE_ERR_ALIGN = 7,     /* float32 src or dst not 4-byte aligned     */
+    MI_RESIZE_ERR_PARAM = 8      /* bad normalisation parameters              */
 };
 
 /* Linear (bilinear) resize; see the header comment for the exact result. */
@@ -92,6 +93,30 @@ int resize_linear(const void *src, void *dst, int batch, int H, int W, int C,
 /* Nearest-neighbour resize (half-pixel centres, rounding half up). */
 int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C,
                    int dtype, int dst_H, int dst_W, void *stream);
+
+/*
+ * Linear resize fused with normalisation, for batches fed to a network.
+ * The resize fused with the step that follows it ("merge" of consecutive
+ * kernels with the same work shape in "Performance Optimization of Object
+ * Tracking Algorithms in OpenCV on GPUs", s4; fusing interpolation with later
+ * processing in hnwysp.cn news/129086 s4.2 and s11, for the batched data
+ * augmentation of s7.2).
+ *
+ * src: uint8, batch x H x W x C (as resize_linear).  dst: float32, either
+ * batch x dst_H x dst_W x C (layout 0, NHWC) or batch x C x dst_H x dst_W
+ * (layout 1, NCHW).  Each element is
+ *     dst = (v * alpha - mean[c]) / std_dev[c]
+ * where v is exactly the uint8 value resize_linear produces; the kernel
+ * evaluates it as one float32 fused multiply-add with scale = alpha / std_dev
+ * and bias = -mean / std_dev computed in double and rounded to float.
+ * mean and std_dev are HOST arrays of C floats, read during the call.
+ * Errors as above, plus MI_RESIZE_ERR_PARAM (mean / std_dev NULL, std_dev
+ * zero or not finite, alpha not finite, layout not 0 / 1) and
+ * MI_RESIZE_ERR_ALIGN (dst not 4-byte aligned).
+ */
+int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W, int C,
+                            int dst_H, int dst_W, float alpha, const float *mean,
+                            const float *std_dev, int layout, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *resize_status_string(int status);

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("resize_linear", "resize_nearest", "resize_status_string",
-              "resize_abi_version", "resize_copy_bytes"):
+              "resize_abi_version", "resize_copy_bytes", "resize_linear_normalize"):
         assert n in names
 
 
@@ -39,8 +39,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert R.resize_abi_version() == 1
-    for code in range(8):
+    assert R.resize_abi_version() == 2
+    for code in range(9):
         s = R.resize_status_string(code)
         assert isinstance(s, str) and s
     assert R.resize_status_string(99) == "unknown status"
@@ -87,3 +87,25 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(R, "_LIB_PATH", "/nonexistent/libmi_resize.so")
     with pytest.raises(RuntimeError, match="not built"):
         R.resize_abi_version()
+
+
+def test_normalize_validation():
+    lib = R._load()
+    f3 = ctypes.c_float * 3
+    mean, std = f3(0.5, 0.5, 0.5), f3(0.25, 0.25, 0.25)
+
+    def norm(src=FAKE_SRC, dst=FAKE_DST, C=3, H=8, W=8, dH=4, dW=4, alpha=1.0, m=mean, s=std, layout=1):
+        return lib.resize_linear_normalize(src, dst, 1, H, W, C, dH, dW, alpha, m, s, layout, None)
+
+    assert norm(src=None) == 1
+    assert norm(H=0) == 2
+    assert norm(C=2) == 3
+    assert norm(m=None) == 8
+    assert norm(s=None) == 8
+    assert norm(layout=2) == 8
+    assert norm(s=f3(0.25, 0.0, 0.25)) == 8
+    assert norm(s=f3(0.25, float("inf"), 0.25)) == 8
+    assert norm(m=f3(0.0, float("nan"), 0.0)) == 8
+    assert norm(alpha=float("nan")) == 8
+    assert norm(dst=FAKE_DST + 2) == 7
+    assert norm(dst=FAKE_SRC + 4) == 5

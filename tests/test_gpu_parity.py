@@ -296,3 +296,59 @@ def test_copy_bytes():
         R.resize_copy_bytes(a, b)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# fused resize + normalisation (uint8 -> float32, NHWC / NCHW)
+# --------------------------------------------------------------------------
+IMAGENET = ((0.485, 0.456, 0.406, 0.5), (0.229, 0.224, 0.225, 0.25))
+
+
+def run_normalize(s, dH, dW, layout, alpha=1 / 255):
+    N, H, W, C = s.shape
+    mean, std = IMAGENET[0][:C], IMAGENET[1][:C]
+    src = torch.from_numpy(s).cuda()
+    shape = (N, dH, dW, C) if layout == "NHWC" else (N, C, dH, dW)
+    dst = torch.empty(shape, dtype=torch.float32, device="cuda")
+    R.resize_linear_normalize(src, dst, mean, std, alpha=alpha, layout=layout)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy(), oracle.resize_linear_normalize(s, dH, dW, alpha, mean, std, layout)
+
+
+def assert_norm_parity(got, want, what):
+    """The uint8 resize inside is exact; the float32 affine step (one FMA with
+    scale and bias rounded to float) is within 3 * 2^-24 relative of the
+    float64 value, so 1e-5 * max(1, |value|) bounds it with margin."""
+    assert got.shape == want.shape, what
+    assert np.isfinite(got).all(), what
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    tol = 1e-5 * np.maximum(1.0, np.abs(want.astype(np.float64)))
+    bad = err > tol
+    assert not bad.any(), "%s: %d elements off, worst %g" % (what, bad.sum(), (err / tol).max())
+
+
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_normalize_thumb_batch(layout):
+    w = WORKLOADS["thumb"]
+    say("case normalize thumb %s" % layout)
+    got, want = run_normalize(make_source(w), w.dH, w.dW, layout)
+    assert_norm_parity(got, want, "normalize thumb " + layout)
+
+
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_normalize_random_shapes(layout, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
+    r = np.random.default_rng(333 + (layout == "NHWC"))
+    for i in range(40):
+        N, H, W, C, dH, dW = random_case(r)
+        say("case normalize %s %s #%d %s" % (layout, path, i, (N, H, W, C, dH, dW)))
+        s = random_image(r, (N, H, W, C), "u8")
+        got, want = run_normalize(s, dH, dW, layout, alpha=float(r.choice([1 / 255, 1.0])))
+        assert_norm_parity(got, want, "normalize #%d" % i)
+    for (N, H, W, C, dH, dW) in EDGE[:12]:
+        say("case normalize edge %s %s %s" % (layout, path, (N, H, W, C, dH, dW)))
+        s = random_image(r, (N, H, W, C), "u8")
+        got, want = run_normalize(s, dH, dW, layout)
+        assert_norm_parity(got, want, "normalize edge %s" % ((N, H, W, C, dH, dW),))

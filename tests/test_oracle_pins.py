@@ -359,3 +359,30 @@ def test_output_within_source_range():
         s = rand_img(r, (1, 9, 9, 1), np.uint8) // 2 + 40
         out = oracle.resize_linear(s, int(r.integers(1, 30)), int(r.integers(1, 30)))
         assert out.min() >= s.min() and out.max() <= s.max()
+
+
+# --------------------------------------------------------------------------
+# fused resize + normalisation: the resize part is the pinned uint8 oracle;
+# these pin the affine map and the layouts
+# --------------------------------------------------------------------------
+def test_normalize_identity_scale_is_plain_normalisation():
+    r = rng(18)
+    s = rand_img(r, (2, 9, 11, 3), np.uint8)
+    mean, std = (0.485, 0.456, 0.406), (0.229, 0.224, 0.225)
+    out = oracle.resize_linear_normalize(s, 9, 11, 1 / 255, mean, std, "NHWC")
+    ref = (s.astype(np.float64) / 255 - np.array(mean)) / np.array(std)
+    assert np.max(np.abs(out - ref)) <= 3e-7
+
+
+def test_normalize_layouts_and_constant():
+    r = rng(19)
+    s = rand_img(r, (3, 13, 7, 4), np.uint8)
+    a = oracle.resize_linear_normalize(s, 5, 17, 1.0, (1, 2, 3, 4), (2, 4, 8, 16), "NHWC")
+    b = oracle.resize_linear_normalize(s, 5, 17, 1.0, (1, 2, 3, 4), (2, 4, 8, 16), "NCHW")
+    assert b.shape == (3, 4, 5, 17) and np.array_equal(a.transpose(0, 3, 1, 2), b)
+    # powers-of-two std and integer mean: exact in float32
+    v = oracle.resize_linear(s, 5, 17).astype(np.float64)
+    assert np.array_equal(a, ((v - np.array([1, 2, 3, 4])) / np.array([2, 4, 8, 16])).astype(np.float32))
+    c = np.full((1, 6, 6, 1), 200, dtype=np.uint8)
+    out = oracle.resize_linear_normalize(c, 10, 3, 1 / 255, (0.5,), (0.25,), "NCHW")
+    assert np.allclose(out, (200 / 255 - 0.5) / 0.25, atol=1e-6, rtol=0)
