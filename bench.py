@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
+    p.add_argument("--graph", type=int, default=0, metavar="B",
+                   help="informational: also time the steps captured B at a time into a HIP "
+                        "graph and replayed (small-image latency)")
     p.add_argument("--no-pipelined", action="store_true",
                    help="skip the extra two-stream pipelined measurement")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -259,6 +262,35 @@ def main():
                      "Gpix_s": round(w.dst_pixels * K / wall2 / 1e9, 3),
                      "GBps": round(pair_bytes * K / wall2 / 1e9, 1)}
 
+    # Informational: B steps captured once into a HIP graph and replayed, which
+    # removes the per-call host cost that bounds tiny images.
+    graphed = None
+    if args.graph > 0:
+        B = args.graph
+        gstream = torch.cuda.Stream(dev)
+        gstream.wait_stream(stream)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gstream):
+            gsh = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(B):
+                j = i % pairs
+                rc = entry(sp[j], dp[j], N, H, W, C, code, dH, dW, gsh)
+                if rc:
+                    raise R.ResizeError(rc, "resize (capture)")
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        reps = max(1, K // B)
+        t0g = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        wall_g = time.perf_counter() - t0g
+        graphed = {"steps_per_graph": B, "replays": reps,
+                   "us_per_step": round(wall_g * 1e6 / (reps * B), 3),
+                   "Gpix_s": round(w.dst_pixels * reps * B / wall_g / 1e9, 3)}
+
     # correctness of what was timed: the last buffer written, vs the oracle
     if not args.no_cpu:
         import oracle
@@ -308,6 +340,8 @@ def main():
     }
     if pipelined:
         line["pipelined_two_streams"] = pipelined
+    if graphed:
+        line["graph_replay"] = graphed
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, src_np, mode, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -352,3 +352,42 @@ def test_normalize_random_shapes(layout, path, monkeypatch):
         s = random_image(r, (N, H, W, C), "u8")
         got, want = run_normalize(s, dH, dW, layout)
         assert_norm_parity(got, want, "normalize edge %s" % ((N, H, W, C, dH, dW),))
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture: the entry points allocate, synchronise and memset
+# nothing, so a sequence of calls can be captured once and replayed (the
+# small-image latency path).  Every replay, with eager work and
+# synchronisation in between, must match the eager results.
+# --------------------------------------------------------------------------
+def test_graph_capture_replay():
+    r = np.random.default_rng(404)
+    cases = [((1, 48, 64, 1), (72, 96), "u8", "linear"), ((2, 30, 40, 3), (15, 20), "u8", "linear"),
+             ((1, 33, 17, 4), (50, 9), "f32", "linear"), ((3, 16, 16, 3), (32, 32), "u8", "nearest"),
+             ((1, 64, 96, 1), (32, 48), "u8", "linear")]
+    srcs, dsts, eager = [], [], []
+    for shape, (dH, dW), dt, mode in cases:
+        s = random_image(r, shape, dt)
+        srcs.append(torch.from_numpy(s).cuda())
+        dsts.append(torch.empty((shape[0], dH, dW, shape[3]), dtype=srcs[-1].dtype, device="cuda"))
+        eager.append(run_oracle(s, dH, dW, mode))
+    say("case graph capture of %d resizes" % len(cases))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the binding up outside the capture
+        for (shape, _, _, mode), a, b in zip(cases, srcs, dsts):
+            (R.resize_linear if mode == "linear" else R.resize_nearest)(a, b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (shape, _, _, mode), a, b in zip(cases, srcs, dsts):
+            (R.resize_linear if mode == "linear" else R.resize_nearest)(a, b)
+    for rep in range(4):
+        for b in dsts:
+            b.fill_(0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (b, want) in enumerate(zip(dsts, eager)):
+            assert_parity(b.cpu().numpy(), want, "graph replay %d case %d" % (rep, i))
