@@ -56,9 +56,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="4k")
     p.add_argument("--mode", default=None, help="linear (default) or nearest")
-    p.add_argument("--op", default="resize", choices=["resize", "normalize"],
+    p.add_argument("--op", default="resize", choices=["resize", "normalize", "crop"],
                    help="normalize: the fused uint8 -> float32 NCHW resize + normalisation "
-                        "(ImageNet mean / std, alpha 1/255) on the same workload")
+                        "(ImageNet mean / std, alpha 1/255) on the same workload; crop: "
+                        "batched crop-then-resize with seeded random-resized-crop regions")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
@@ -171,6 +172,19 @@ def main():
     tdt = torch.uint8 if w.dtype == "u8" else torch.float32
     src0 = torch.from_numpy(src_np).to(dev)
     fused = args.op == "normalize"
+    cropped = args.op == "crop"
+    crops_np = None
+    if cropped:
+        rng = np.random.default_rng(w.seed + 77)
+        crops = []
+        for _ in range(w.batch):   # area 8-100 %, aspect 3/4 - 4/3
+            area = w.H * w.W * rng.uniform(0.08, 1.0)
+            ar = np.exp(rng.uniform(np.log(3 / 4), np.log(4 / 3)))
+            cw = int(min(w.W, max(1, round(np.sqrt(area * ar)))))
+            ch = int(min(w.H, max(1, round(np.sqrt(area / ar)))))
+            crops.append((int(rng.integers(0, w.W - cw + 1)), int(rng.integers(0, w.H - ch + 1)), cw, ch))
+        crops_np = np.array(crops, dtype=np.int32)
+        crops_dev = torch.from_numpy(crops_np).to(dev)
     if fused:
         if w.dtype != "u8" or mode != "linear":
             sys.exit("--op normalize needs a uint8 linear workload")
@@ -179,7 +193,10 @@ def main():
         tdt_out = torch.float32
     else:
         dst_shape, dst_bytes, tdt_out = w.dst_shape, w.dst_bytes, tdt
-    pair_bytes = w.src_bytes + dst_bytes
+    src_bytes = w.src_bytes
+    if cropped:   # only the crops are read
+        src_bytes = int(sum(int(c[2]) * int(c[3]) for c in crops_np)) * w.C * w.itemsize
+    pair_bytes = src_bytes + dst_bytes
     pairs = 1 if args.warm else max(2, -(-2 * INFINITY_CACHE_BYTES // pair_bytes))
     srcs = [src0] + [src0.clone() for _ in range(pairs - 1)]
     dsts = [torch.empty(dst_shape, dtype=tdt_out, device=dev) for _ in range(pairs)]
@@ -199,6 +216,14 @@ def main():
 
         def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
             return base(s_, d_, N_, H_, W_, C_, dH_, dW_, 1.0 / 255.0, mean_c, std_c, 1, sh_)
+    if cropped:
+        if mode != "linear":
+            sys.exit("--op crop is linear only")
+        roi_entry = lib.resize_linear_roi
+        roi_ptr = crops_dev.data_ptr()
+
+        def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
+            return roi_entry(s_, d_, N_, H_, W_, C_, code_, roi_ptr, dH_, dW_, sh_)
     sh = stream.cuda_stream
     sp = [t.data_ptr() for t in srcs]
     dp = [t.data_ptr() for t in dsts]
@@ -295,7 +320,10 @@ def main():
     if not args.no_cpu:
         import oracle
         got = dsts[(K - 1) % pairs].cpu().numpy()
-        if fused:
+        if cropped:
+            ref = oracle.resize_linear_roi(src_np, crops_np, w.dH, w.dW)
+            ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
+        elif fused:
             ref = oracle.resize_linear_normalize(src_np, w.dH, w.dW, 1 / 255, (0.485, 0.456, 0.406, 0.5)[:w.C],
                                                  (0.229, 0.224, 0.225, 0.25)[:w.C], "NCHW")
             ok = bool((np.abs(got - ref) <= 1e-5 * np.maximum(1.0, np.abs(ref))).all())
@@ -305,7 +333,7 @@ def main():
         if not ok:
             sys.exit("bench output disagrees with the oracle")
 
-    traffic = None if fused else traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode)))
+    traffic = None if (fused or cropped) else traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode)))
     line = {
         "metric": "bilinear resize Gpix/s + HBM GB/s (% of peak), RGB u8 4K->1080p, 1 GPU",
         "value": round(gpix, 3),
@@ -322,7 +350,7 @@ def main():
         "config": {
             "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s%s" % (
                 w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode,
-                " + normalize to f32 NCHW" if fused else ""),
+                " + normalize to f32 NCHW" if fused else (" of random crops" if cropped else "")),
             "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
             "mode": mode, "cache": "warm (1 pair)" if args.warm else "cold (%d rotating pairs)" % pairs,
         },
@@ -342,7 +370,7 @@ def main():
         line["pipelined_two_streams"] = pipelined
     if graphed:
         line["graph_replay"] = graphed
-    if not args.no_cpu:
+    if not args.no_cpu and args.op == "resize":
         line["cpu_baseline"] = cpu_baseline(w, src_np, mode, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -23,7 +23,8 @@ import ctypes
 import os
 
 __all__ = [
-    "resize", "resize_linear", "resize_nearest", "resize_linear_normalize", "resize_copy_bytes",
+    "resize", "resize_linear", "resize_nearest", "resize_linear_normalize", "resize_linear_roi",
+    "resize_copy_bytes",
     "resize_status_string", "resize_abi_version", "library_path", "ResizeError",
     "U8", "F32",
 ]
@@ -33,7 +34,7 @@ _LIB_PATH = os.path.join(_PKG, "libmi_resize.so")
 
 U8 = 0
 F32 = 1
-_ABI_VERSION = 2
+_ABI_VERSION = 3
 
 _lib = None
 
@@ -74,6 +75,8 @@ def _load():
     lib.resize_linear_normalize.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float,
                                             fp, fp, ci, vp]
     lib.resize_linear_normalize.restype = ci
+    lib.resize_linear_roi.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp, ci, ci, vp]
+    lib.resize_linear_roi.restype = ci
     if lib.resize_abi_version() != _ABI_VERSION:
         raise RuntimeError("libmi_resize.so ABI version %d, binding expects %d"
                            % (lib.resize_abi_version(), _ABI_VERSION))
@@ -192,6 +195,26 @@ def resize_linear_normalize(src, dst, mean, std, alpha=1.0 / 255.0, layout="NCHW
                                          _stream_handle(stream, src.device))
     if rc != 0:
         raise ResizeError(rc, "resize_linear_normalize")
+    return dst
+
+
+def resize_linear_roi(src, dst, rois, stream=None):
+    """Batched crop-then-resize: image n's region ``rois[n] = (x, y, w, h)``
+    (an int32 CUDA tensor of shape (N, 4), read on the device and clamped into
+    the image) is resized linearly into ``dst[n]`` (same dtype, (N,) dst_H x
+    dst_W x C)."""
+    import torch
+    N, H, W, C = _nhwc(src, "src")
+    N2, dH, dW, C2 = _nhwc(dst, "dst")
+    if (N2, C2) != (N, C) or src.dim() != dst.dim() or src.dtype != dst.dtype:
+        raise ValueError("src %s / dst %s mismatch" % (tuple(src.shape), tuple(dst.shape)))
+    if (not isinstance(rois, torch.Tensor) or rois.dtype != torch.int32 or rois.device != src.device
+            or not rois.is_contiguous() or tuple(rois.shape) != (N, 4)):
+        raise ValueError("rois must be a contiguous int32 tensor of shape (%d, 4) on %s" % (N, src.device))
+    rc = _load().resize_linear_roi(src.data_ptr(), dst.data_ptr(), N, H, W, C, _dtype_code(src),
+                                   rois.data_ptr(), dH, dW, _stream_handle(stream, src.device))
+    if rc != 0:
+        raise ResizeError(rc, "resize_linear_roi")
     return dst
 
 

@@ -82,22 +82,23 @@ int launched()
     return hipGetLastError() == hipSuccess ? MI_RESIZE_OK : MI_RESIZE_ERR_HIP;
 }
 
-template <typename T, int C, int OUT = kOutSame>
+template <typename T, int C, int OUT = kOutSame, bool ROI = false>
 int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                          hipStream_t st, const Affine &aff = Affine{})
+                          hipStream_t st, const Affine &aff = Affine{},
+                          const int32_t *rois = nullptr)
 {
     const long long rows = (long long)batch * dH;
     const Grid g = band_grid(rows, dW);
     const bool pix4 = OUT == kOutSame && C == 4 && aligned(src, 4 * sizeof(T)) &&
                       aligned(dst, 4 * sizeof(T));
     if (pix4) {
-        hipLaunchKernelGGL((linear_generic<T, C, C == 4 && OUT == kOutSame, OUT>), dim3(g.blocks), dim3(kBlock), 0,
-                           st, (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block,
-                           g.col_blocks, aff);
+        hipLaunchKernelGGL((linear_generic<T, C, C == 4 && OUT == kOutSame, OUT, ROI>),
+                           dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W, dH, dW,
+                           rows, g.rows_per_block, g.col_blocks, aff, rois);
     } else {
-        hipLaunchKernelGGL((linear_generic<T, C, false, OUT>), dim3(g.blocks), dim3(kBlock), 0,
-                           st, (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block,
-                           g.col_blocks, aff);
+        hipLaunchKernelGGL((linear_generic<T, C, false, OUT, ROI>), dim3(g.blocks), dim3(kBlock),
+                           0, st, (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block,
+                           g.col_blocks, aff, rois);
     }
     return launched();
 }
@@ -162,24 +163,26 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, SegPlan
     return true;
 }
 
-template <typename T, int C, bool NEAREST, int OUT = kOutSame>
+template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false>
 bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                hipStream_t st, int &rc, const Affine &aff = Affine{})
+                hipStream_t st, int &rc, const Affine &aff = Affine{},
+                const int32_t *rois = nullptr)
 {
     const long long rows = (long long)batch * dH;
     SegPlan pl;
+    // a crop is at most W wide, so the whole-image bound covers every crop
     if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, pl)) return false;
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8
     const int per_lane = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src,
                            dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
-                           (long long)batch * H * W * C, aff);
+                           (long long)batch * H * W * C, aff, rois);
     };
-    if (per_lane <= 1) go(rowseg<T, C, NEAREST, 1, OUT>);
-    else if (per_lane <= 2) go(rowseg<T, C, NEAREST, 2, OUT>);
-    else if (per_lane <= 4) go(rowseg<T, C, NEAREST, 4, OUT>);
-    else go(rowseg<T, C, NEAREST, 8, OUT>);
+    if (per_lane <= 1) go(rowseg<T, C, NEAREST, 1, OUT, ROI>);
+    else if (per_lane <= 2) go(rowseg<T, C, NEAREST, 2, OUT, ROI>);
+    else if (per_lane <= 4) go(rowseg<T, C, NEAREST, 4, OUT, ROI>);
+    else go(rowseg<T, C, NEAREST, 8, OUT, ROI>);
     rc = launched();
     return true;
 }
@@ -273,6 +276,21 @@ int normalize_dispatch(const void *src, float *dst, int batch, int H, int W, int
         if (try_rowseg<uint8_t, C, false, OUT>(src, dst, batch, H, W, dH, dW, st, rc, aff))
             return rc;
     return launch_linear_generic<uint8_t, C, OUT>(src, dst, batch, H, W, dH, dW, st, aff);
+}
+
+template <typename T, int C>
+int roi_dispatch(const void *src, void *dst, int batch, int H, int W, const int32_t *rois,
+                 int dH, int dW, hipStream_t st)
+{
+    const Path path = path_override();
+    int rc;
+    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    if (path == Path::RowSeg || (path == Path::Auto && !small))
+        if (try_rowseg<T, C, false, kOutSame, true>(src, dst, batch, H, W, dH, dW, st, rc,
+                                                     Affine{}, rois))
+            return rc;
+    return launch_linear_generic<T, C, kOutSame, true>(src, dst, batch, H, W, dH, dW, st,
+                                                       Affine{}, rois);
 }
 
 }  // namespace
@@ -376,6 +394,28 @@ int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W
     case 1: return normalize_dispatch<1, kOutNormNCHW>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
     case 3: return normalize_dispatch<3, kOutNormNCHW>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
     default: return normalize_dispatch<4, kOutNormNCHW>(src, dst, batch, H, W, dst_H, dst_W, st, aff);
+    }
+}
+
+int resize_linear_roi(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                      const int32_t *rois, int dst_H, int dst_W, void *stream)
+{
+    const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
+    if (rc != MI_RESIZE_OK) return rc;
+    if (!rois) return MI_RESIZE_ERR_NULL;
+    if (!aligned(rois, 4)) return MI_RESIZE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == MI_RESIZE_U8) {
+        switch (C) {
+        case 1: return roi_dispatch<uint8_t, 1>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
+        case 3: return roi_dispatch<uint8_t, 3>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
+        default: return roi_dispatch<uint8_t, 4>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
+        }
+    }
+    switch (C) {
+    case 1: return roi_dispatch<float, 1>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
+    case 3: return roi_dispatch<float, 3>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
+    default: return roi_dispatch<float, 4>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
     }
 }
 

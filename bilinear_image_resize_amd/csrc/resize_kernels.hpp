@@ -121,6 +121,24 @@ struct Affine {
     float bias[4];
 };
 
+// Region of interest of image n: crop {x, y, w, h} from a device array of
+// int32 quadruples, clamped into the image (x in [0, W-1], w in [1, W - x],
+// likewise y / h), so any values are safe to read through.
+struct Crop {
+    int x, y, w, h;
+};
+
+__device__ __forceinline__ Crop load_crop(const int32_t *rois, long long n, int H, int W)
+{
+    const int32_t *q = rois + 4 * n;
+    Crop c;
+    c.x = min(max((int)q[0], 0), W - 1);
+    c.y = min(max((int)q[1], 0), H - 1);
+    c.w = min(max((int)q[2], 1), W - c.x);
+    c.h = min(max((int)q[3], 1), H - c.y);
+    return c;
+}
+
 // --------------------------------------------------------------------------
 // Generic linear resize, any scale, C in {1, 3, 4}.  Grid: 1-D,
 // blockIdx = row_block * col_blocks + col_block.  A block covers kBlock
@@ -128,10 +146,11 @@ struct Affine {
 // output pixel per row.  PIX4: C == 4 and the buffers are aligned so that a
 // whole pixel moves as one 4-byte (u8) or 16-byte (f32) access.
 // --------------------------------------------------------------------------
-template <typename T, int C, bool PIX4, int OUT = kOutSame>
+template <typename T, int C, bool PIX4, int OUT = kOutSame, bool ROI = false>
 __global__ __launch_bounds__(kBlock) void linear_generic(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
-    long long rows_total, int rows_per_block, int col_blocks, Affine aff)
+    long long rows_total, int rows_per_block, int col_blocks, Affine aff,
+    const int32_t *__restrict__ rois)
 {
     T *const dst = (T *)dst_v;
     float *const dstf = (float *)dst_v;
@@ -139,13 +158,6 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
     const long long rb = blockIdx.x / (unsigned)col_blocks;
     const int x = cb * kBlock + (int)threadIdx.x;
     if (x >= dW) return;
-
-    const Tap tx = axis_tap(x, W, dW);
-    const int xa = tx.a * C, xb = tx.b * C;
-    unsigned wx1 = 0;
-    float wxf = 0.f;
-    if constexpr (sizeof(T) == 1) wx1 = weight11(tx);
-    else wxf = weightf(tx);
 
     long long g = rb * rows_per_block;
     long long g_end = g + rows_per_block;
@@ -155,11 +167,26 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
     const size_t img_elems = (size_t)H * W * C;
     const size_t row_elems = (size_t)W * C;
 
+    // the source region resized: the whole image or image n's crop
+    Crop crop{0, 0, W, H};
+    if constexpr (ROI) crop = load_crop(rois, n, H, W);
+    int xa, xb;
+    unsigned wx1 = 0;
+    float wxf = 0.f;
+    auto column = [&]() {
+        const Tap tx = axis_tap(x, crop.w, dW);
+        xa = (crop.x + tx.a) * C;
+        xb = (crop.x + tx.b) * C;
+        if constexpr (sizeof(T) == 1) wx1 = weight11(tx);
+        else wxf = weightf(tx);
+    };
+    column();
+
     for (; g < g_end; ++g) {
-        const Tap ty = axis_tap(dy, H, dH);
+        const Tap ty = axis_tap(dy, crop.h, dH);
         const T *img = src + (size_t)n * img_elems;
-        const T *r0 = img + (size_t)ty.a * row_elems;
-        const T *r1 = img + (size_t)ty.b * row_elems;
+        const T *r0 = img + (size_t)(crop.y + ty.a) * row_elems;
+        const T *r1 = img + (size_t)(crop.y + ty.b) * row_elems;
         T *out = dst + ((size_t)g * dW + x) * C;
         if constexpr (sizeof(T) == 1) {
             const unsigned wy1 = weight11(ty);
@@ -212,7 +239,16 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                     out[k] = blend_f32(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k], wxf, wyf);
             }
         }
-        if (++dy == dH) { dy = 0; ++n; }
+        if (++dy == dH) {
+            dy = 0;
+            ++n;
+            if constexpr (ROI) {
+                if (g + 1 < g_end) {
+                    crop = load_crop(rois, n, H, W);
+                    column();
+                }
+            }
+        }
     }
 }
 
@@ -642,10 +678,11 @@ struct RowStepper {
     }
 };
 
-template <typename T, int C, bool NEAREST, int KMAX, int OUT = kOutSame>
+template <typename T, int C, bool NEAREST, int KMAX, int OUT = kOutSame, bool ROI = false>
 __global__ __launch_bounds__(kSegLanes) void rowseg(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
-    long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff)
+    long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff,
+    const int32_t *__restrict__ rois)
 {
     T *const dst = (T *)dst_v;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -657,51 +694,62 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
     const int x0 = wx0 + lane * PX;               // this lane's first output column
     const int valid_px = max(0, min(PX, dW - x0));
 
-    // Source columns touched by the segment, and this lane's column table:
-    // byte offset of tap a from column sa, whether tap b is the next column
-    // (it is not only where both taps clamp to the last column), and the
-    // weight of tap b.
-    int sa, sb;
-    if constexpr (NEAREST) {
-        sa = nearest_index(wx0, W, dW);
-        sb = nearest_index(wx1, W, dW);
-    } else {
-        sa = axis_tap(wx0, W, dW).a;
-        sb = axis_tap(wx1, W, dW).b;
-    }
-    int toff[PX];
-    bool tnext[PX];
-    unsigned tw[PX];
-    float twf[PX];
-#pragma unroll
-    for (int p = 0; p < PX; ++p) {
-        const int x = min(x0 + p, dW - 1);
-        if constexpr (NEAREST) {
-            toff[p] = (nearest_index(x, W, dW) - sa) * PB;
-            tnext[p] = false;
-            tw[p] = 0;
-            twf[p] = 0.f;
-        } else {
-            const Tap t = axis_tap(x, W, dW);
-            toff[p] = (t.a - sa) * PB;
-            tnext[p] = t.b != t.a;
-            if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
-            else twf[p] = weightf(t);
-        }
-    }
-    const int seg_bytes = (sb - sa + 1) * PB;
-    const uint8_t *lo = (const uint8_t *)src;
-    const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
-    const size_t row_bytes = (size_t)W * PB;
-    T *const out_lane = dst + (size_t)x0 * C;
-
     long long g = (long long)blockIdx.y * rows_per_block;
     long long g_end = g + rows_per_block;
     if (g_end > rows_total) g_end = rows_total;
     long long n = g / dH;
     int dy = (int)(g - n * dH);
+
+    // The source region resized: the whole image, or image n's crop.
+    Crop crop{0, 0, W, H};
+    if constexpr (ROI) crop = load_crop(rois, n, H, W);
+
+    // Source columns touched by the segment, and this lane's column table:
+    // byte offset of tap a from column sa, whether tap b is the next column
+    // (it is not only where both taps clamp to the last column), and the
+    // weight of tap b.  Recomputed when a crop changes with the image.
+    int sa, sb;
+    int toff[PX];
+    bool tnext[PX];
+    unsigned tw[PX];
+    float twf[PX];
+    auto column_table = [&]() {
+        const int cw = crop.w;
+        if constexpr (NEAREST) {
+            sa = nearest_index(wx0, cw, dW);
+            sb = nearest_index(wx1, cw, dW);
+        } else {
+            sa = axis_tap(wx0, cw, dW).a;
+            sb = axis_tap(wx1, cw, dW).b;
+        }
+#pragma unroll
+        for (int p = 0; p < PX; ++p) {
+            const int x = min(x0 + p, dW - 1);
+            if constexpr (NEAREST) {
+                toff[p] = (nearest_index(x, cw, dW) - sa) * PB;
+                tnext[p] = false;
+                tw[p] = 0;
+                twf[p] = 0.f;
+            } else {
+                const Tap t = axis_tap(x, cw, dW);
+                toff[p] = (t.a - sa) * PB;
+                tnext[p] = t.b != t.a;
+                if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
+                else twf[p] = weightf(t);
+            }
+        }
+        sa += crop.x;
+        sb += crop.x;
+    };
+    column_table();
+    int seg_bytes = (sb - sa + 1) * PB;
+    const uint8_t *lo = (const uint8_t *)src;
+    const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
+    const size_t row_bytes = (size_t)W * PB;
+    T *const out_lane = dst + (size_t)x0 * C;
+
     RowStepper ys;
-    ys.init(dy, H, dH);
+    ys.init(dy, crop.h, dH);
     // global source row held in each LDS slot, and its offset there
     long long held0 = -1, held1 = -1;
     int mis0 = 0, mis1 = 0;
@@ -710,21 +758,22 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
         int ya, yb;
         unsigned wy1 = 0;
         float wyf = 0.f;
+        const int Hc = crop.h;
         if constexpr (NEAREST) {
             // nearest row: floor((2dy + 1) H / (2 dH)) = floor((num + dH) / den)
             long long k = ys.q + ((ys.r + dH) >= ys.den ? 1 : 0);
-            ya = yb = (int)(k > H - 1 ? H - 1 : (k < 0 ? 0 : k));
+            ya = yb = (int)(k > Hc - 1 ? Hc - 1 : (k < 0 ? 0 : k));
         } else {
             const long long q = ys.q;
-            ya = (int)(q < 0 ? 0 : (q > H - 1 ? H - 1 : q));
-            yb = (int)(q + 1 < 0 ? 0 : (q + 1 > H - 1 ? H - 1 : q + 1));
+            ya = (int)(q < 0 ? 0 : (q > Hc - 1 ? Hc - 1 : q));
+            yb = (int)(q + 1 < 0 ? 0 : (q + 1 > Hc - 1 ? Hc - 1 : q + 1));
             Tap t;
             t.r = (int)ys.r;
             t.den = (int)ys.den;
             if constexpr (sizeof(T) == 1) wy1 = weight11(t);
             else wyf = weightf(t);
         }
-        const long long ra = n * H + ya, rb = n * H + yb;
+        const long long ra = n * H + crop.y + ya, rb = n * H + crop.y + yb;
         int sa_slot = held0 == ra ? 0 : (held1 == ra ? 1 : -1);
         int sb_slot = held0 == rb ? 0 : (held1 == rb ? 1 : -1);
         const bool need_a = sa_slot < 0;
@@ -831,7 +880,14 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
         if (++dy == dH) {
             dy = 0;
             ++n;
-            ys.init(0, H, dH);
+            if constexpr (ROI) {
+                if (g + 1 < g_end) {
+                    crop = load_crop(rois, n, H, W);
+                    column_table();
+                    seg_bytes = (sb - sa + 1) * PB;
+                }
+            }
+            ys.init(0, crop.h, dH);
         } else {
             ys.next();
         }

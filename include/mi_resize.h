@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MI_RESIZE_ABI_VERSION 2
+#define MI_RESIZE_ABI_VERSION 3
 
 enum mi_resize_dtype {
     MI_RESIZE_U8 = 0,   /* uint8_t elements  */
@@ -117,6 +117,25 @@ int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C,
 int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W, int C,
                             int dst_H, int dst_W, float alpha, const float *mean,
                             const float *std_dev, int layout, void *stream);
+
+/*
+ * Batched crop-then-resize: image n's region {x, y, w, h} (columns x .. x+w-1,
+ * rows y .. y+h-1) is resized linearly to dst_H x dst_W, exactly as
+ * resize_linear would resize that crop taken as an image of its own
+ * (half-pixel centres and clamp-to-edge relative to the crop).  This is the
+ * "random crop then resize" of batched data augmentation (hnwysp.cn
+ * news/129086 s7.2) and the differing input regions of multi-stream video
+ * (s7.1).
+ *
+ * rois: DEVICE pointer to batch x 4 int32 {x, y, w, h}, 4-byte aligned,
+ * read by the kernels (so it may be written by earlier work on the same
+ * stream).  Values are clamped into the image on the device: x to [0, W-1],
+ * w to [1, W - x], y and h likewise; no value can make a kernel read outside
+ * src.  Other arguments, layout and errors as resize_linear (MI_RESIZE_ERR_NULL
+ * for a NULL rois, MI_RESIZE_ERR_ALIGN for a misaligned one).
+ */
+int resize_linear_roi(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                      const int32_t *rois, int dst_H, int dst_W, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *resize_status_string(int status);

@@ -136,6 +136,30 @@ def resize_linear_normalize(src: np.ndarray, dH: int, dW: int, alpha, mean, std,
     raise ValueError("layout must be NCHW or NHWC")
 
 
+def clamp_roi(roi, H: int, W: int):
+    """The crop {x, y, w, h} clamped into an H x W image: x to [0, W-1],
+    w to [1, W - x], y and h likewise (the library's documented rule)."""
+    x, y, w, h = (int(v) for v in roi)
+    x = min(max(x, 0), W - 1)
+    y = min(max(y, 0), H - 1)
+    w = min(max(w, 1), W - x)
+    h = min(max(h, 1), H - y)
+    return x, y, w, h
+
+
+def resize_linear_roi(src: np.ndarray, rois, dH: int, dW: int) -> np.ndarray:
+    """Crop then resize, per image: image n's clamped crop is cut out and
+    resized with resize_linear as an image of its own (the random crop then
+    resize of batched augmentation, hnwysp.cn news/129086 s7.2)."""
+    src = _as_nhwc(src)
+    N, H, W, C = src.shape
+    out = np.empty((N, dH, dW, C), dtype=src.dtype)
+    for n in range(N):
+        x, y, w, h = clamp_roi(rois[n], H, W)
+        out[n] = resize_linear(np.ascontiguousarray(src[n:n + 1, y:y + h, x:x + w]), dH, dW)[0]
+    return out
+
+
 def resize_nearest(src: np.ndarray, dH: int, dW: int, rows=None) -> np.ndarray:
     """Nearest-neighbour resize of an NHWC array (any element type) to dH x dW."""
     src = _as_nhwc(src)

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("resize_linear", "resize_nearest", "resize_status_string",
-              "resize_abi_version", "resize_copy_bytes", "resize_linear_normalize"):
+              "resize_abi_version", "resize_copy_bytes", "resize_linear_normalize",
+              "resize_linear_roi"):
         assert n in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert R.resize_abi_version() == 2
+    assert R.resize_abi_version() == 3
     for code in range(9):
         s = R.resize_status_string(code)
         assert isinstance(s, str) and s
@@ -109,3 +110,17 @@ def test_normalize_validation():
     assert norm(alpha=float("nan")) == 8
     assert norm(dst=FAKE_DST + 2) == 7
     assert norm(dst=FAKE_SRC + 4) == 5
+
+
+def test_roi_validation():
+    lib = R._load()
+
+    def roi(src=FAKE_SRC, dst=FAKE_DST, rois=0x30000000, C=3, dtype=0, H=8):
+        return lib.resize_linear_roi(src, dst, 2, H, 8, C, dtype, rois, 4, 4, None)
+
+    assert roi(src=None) == 1
+    assert roi(rois=None) == 1
+    assert roi(rois=0x30000002) == 7
+    assert roi(C=2) == 3
+    assert roi(dtype=5) == 4
+    assert roi(H=0) == 2

@@ -391,3 +391,60 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
         for i, (b, want) in enumerate(zip(dsts, eager)):
             assert_parity(b.cpu().numpy(), want, "graph replay %d case %d" % (rep, i))
+
+
+# --------------------------------------------------------------------------
+# batched crop-then-resize with per-image regions
+# --------------------------------------------------------------------------
+def random_crops(r, N, H, W, bad=False):
+    """Random-resized-crop style regions (area 8-100 %, aspect 3/4-4/3); with
+    bad=True some are partly or wholly outside the image (clamped)."""
+    out = []
+    for _ in range(N):
+        area = H * W * r.uniform(0.08, 1.0)
+        ar = np.exp(r.uniform(np.log(3 / 4), np.log(4 / 3)))
+        w = int(min(W, max(1, round(np.sqrt(area * ar)))))
+        h = int(min(H, max(1, round(np.sqrt(area / ar)))))
+        x = int(r.integers(0, W - w + 1))
+        y = int(r.integers(0, H - h + 1))
+        if bad and r.random() < 0.5:
+            x, y = x + int(r.integers(-W, W)), y + int(r.integers(-H, H))
+            w, h = w + int(r.integers(-W, W)), h + int(r.integers(-H, H))
+        out.append((x, y, w, h))
+    return np.array(out, dtype=np.int32)
+
+
+def run_roi(s, rois, dH, dW):
+    src = torch.from_numpy(s).cuda()
+    N, H, W, C = s.shape
+    dst = torch.empty((N, dH, dW, C), dtype=src.dtype, device="cuda")
+    R.resize_linear_roi(src, dst, torch.from_numpy(rois).cuda())
+    torch.cuda.synchronize()
+    return dst.cpu().numpy()
+
+
+def test_roi_thumb_batch():
+    w = WORKLOADS["thumb"]
+    r = np.random.default_rng(515)
+    s = make_source(w)
+    rois = random_crops(r, w.batch, w.H, w.W)
+    say("case roi thumb batch")
+    assert_parity(run_roi(s, rois, w.dH, w.dW), oracle.resize_linear_roi(s, rois, w.dH, w.dW), "roi thumb")
+
+
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_roi_random(dtype, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
+    r = np.random.default_rng(616 + (dtype == "f32"))
+    for i in range(25):
+        N = int(r.integers(1, 9))
+        C = int(r.choice([1, 3, 4]))
+        H, W = (int(v) for v in r.integers(1, 200, size=2))
+        dH, dW = (int(v) for v in r.integers(1, 300, size=2))
+        s = random_image(r, (N, H, W, C), dtype)
+        rois = random_crops(r, N, H, W, bad=(i % 3 == 0))
+        say("case roi %s %s #%d %s" % (dtype, path, i, (N, H, W, C, dH, dW)))
+        assert_parity(run_roi(s, rois, dH, dW), oracle.resize_linear_roi(s, rois, dH, dW),
+                      "roi #%d" % i)

@@ -386,3 +386,30 @@ def test_normalize_layouts_and_constant():
     c = np.full((1, 6, 6, 1), 200, dtype=np.uint8)
     out = oracle.resize_linear_normalize(c, 10, 3, 1 / 255, (0.5,), (0.25,), "NCHW")
     assert np.allclose(out, (200 / 255 - 0.5) / 0.25, atol=1e-6, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# crop then resize: a crop of a ramp is a ramp (offset by the crop corner),
+# so the result is the ramp at crop corner + the crop's half-pixel coordinate
+# --------------------------------------------------------------------------
+def test_roi_of_ramp_is_shifted_ramp():
+    H, W = 40, 50
+    ys, xs = np.mgrid[0:H, 0:W]
+    img = (xs / 64.0 + ys / 128.0).astype(np.float32)[None, :, :, None]
+    rois = [(3, 5, 20, 17), (0, 0, 50, 40), (49, 39, 7, 9), (-4, 10, 30, 100)]
+    src = np.repeat(img, len(rois), axis=0)
+    out = oracle.resize_linear_roi(src, rois, 11, 13)
+    for n, roi in enumerate(rois):
+        x0, y0, w, h = oracle.clamp_roi(roi, H, W)
+        for dy in range(11):
+            sy = float(src_coord(dy, h, 11)) + y0
+            for dx in range(13):
+                sx = float(src_coord(dx, w, 13)) + x0
+                assert abs(out[n, dy, dx, 0] - (sx / 64.0 + sy / 128.0)) <= 1e-6
+
+
+def test_roi_full_image_is_plain_resize():
+    r = rng(20)
+    s = rand_img(r, (3, 17, 23, 3), np.uint8)
+    full = [(0, 0, 23, 17)] * 3
+    assert np.array_equal(oracle.resize_linear_roi(s, full, 9, 31), oracle.resize_linear(s, 9, 31))
