@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
+    p.add_argument("--border", default="clamp", choices=["clamp", "mirror", "wrap"],
+                   help="border rule for --op resize (linear): mirror / wrap use resize_linear_border")
     p.add_argument("--graph", type=int, default=0, metavar="B",
                    help="informational: also time the steps captured B at a time into a HIP "
                         "graph and replayed (small-image latency)")
@@ -216,6 +218,14 @@ def main():
 
         def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
             return base(s_, d_, N_, H_, W_, C_, dH_, dW_, 1.0 / 255.0, mean_c, std_c, 1, sh_)
+    if args.border != "clamp":
+        if mode != "linear" or fused or cropped:
+            sys.exit("--border applies to the plain linear resize")
+        border_entry = lib.resize_linear_border
+        border_code = {"mirror": 1, "wrap": 2}[args.border]
+
+        def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
+            return border_entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, border_code, sh_)
     if cropped:
         if mode != "linear":
             sys.exit("--op crop is linear only")
@@ -328,12 +338,16 @@ def main():
                                                  (0.229, 0.224, 0.225, 0.25)[:w.C], "NCHW")
             ok = bool((np.abs(got - ref) <= 1e-5 * np.maximum(1.0, np.abs(ref))).all())
         else:
-            ref = (oracle.resize_linear if mode == "linear" else oracle.resize_nearest)(src_np, w.dH, w.dW)
+            if mode == "linear":
+                ref = oracle.resize_linear(src_np, w.dH, w.dW, border=args.border)
+            else:
+                ref = oracle.resize_nearest(src_np, w.dH, w.dW)
             ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
         if not ok:
             sys.exit("bench output disagrees with the oracle")
 
-    traffic = None if (fused or cropped) else traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode)))
+    traffic = (None if (fused or cropped or args.border != "clamp")
+               else traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode))))
     line = {
         "metric": "bilinear resize Gpix/s + HBM GB/s (% of peak), RGB u8 4K->1080p, 1 GPU",
         "value": round(gpix, 3),
@@ -350,7 +364,8 @@ def main():
         "config": {
             "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s%s" % (
                 w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode,
-                " + normalize to f32 NCHW" if fused else (" of random crops" if cropped else "")),
+                " + normalize to f32 NCHW" if fused else (" of random crops" if cropped else
+                ("" if args.border == "clamp" else ", %s border" % args.border))),
             "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
             "mode": mode, "cache": "warm (1 pair)" if args.warm else "cold (%d rotating pairs)" % pairs,
         },

@@ -24,6 +24,7 @@ import os
 
 __all__ = [
     "resize", "resize_linear", "resize_nearest", "resize_linear_normalize", "resize_linear_roi",
+    "resize_linear_border",
     "resize_copy_bytes",
     "resize_status_string", "resize_abi_version", "library_path", "ResizeError",
     "U8", "F32",
@@ -34,7 +35,7 @@ _LIB_PATH = os.path.join(_PKG, "libmi_resize.so")
 
 U8 = 0
 F32 = 1
-_ABI_VERSION = 3
+_ABI_VERSION = 4
 
 _lib = None
 
@@ -77,6 +78,8 @@ def _load():
     lib.resize_linear_normalize.restype = ci
     lib.resize_linear_roi.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp, ci, ci, vp]
     lib.resize_linear_roi.restype = ci
+    lib.resize_linear_border.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.resize_linear_border.restype = ci
     if lib.resize_abi_version() != _ABI_VERSION:
         raise RuntimeError("libmi_resize.so ABI version %d, binding expects %d"
                            % (lib.resize_abi_version(), _ABI_VERSION))
@@ -215,6 +218,26 @@ def resize_linear_roi(src, dst, rois, stream=None):
                                    rois.data_ptr(), dH, dW, _stream_handle(stream, src.device))
     if rc != 0:
         raise ResizeError(rc, "resize_linear_roi")
+    return dst
+
+
+BORDERS = {"clamp": 0, "mirror": 1, "wrap": 2}
+
+
+def resize_linear_border(src, dst, border="mirror", stream=None):
+    """Linear resize with a border rule for coordinates beyond the outermost
+    pixel centres: "clamp" (as resize_linear), "mirror" (reflect about the
+    edge pixel centres) or "wrap" (periodic image)."""
+    if border not in BORDERS:
+        raise ValueError("border must be one of %s" % sorted(BORDERS))
+    N, H, W, C = _nhwc(src, "src")
+    N2, dH, dW, C2 = _nhwc(dst, "dst")
+    if (N2, C2) != (N, C) or src.dim() != dst.dim() or src.dtype != dst.dtype:
+        raise ValueError("src %s / dst %s mismatch" % (tuple(src.shape), tuple(dst.shape)))
+    rc = _load().resize_linear_border(src.data_ptr(), dst.data_ptr(), N, H, W, C, _dtype_code(src),
+                                      dH, dW, BORDERS[border], _stream_handle(stream, src.device))
+    if rc != 0:
+        raise ResizeError(rc, "resize_linear_border")
     return dst
 
 

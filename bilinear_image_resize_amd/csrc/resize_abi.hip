@@ -293,6 +293,28 @@ int roi_dispatch(const void *src, void *dst, int batch, int H, int W, const int3
                                                        Affine{}, rois);
 }
 
+template <typename T, int C>
+int border_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                    int border, hipStream_t st)
+{
+    const long long rows = (long long)batch * dH;
+    const Grid g = band_grid(rows, dW);
+    const bool pix4 = C == 4 && aligned(src, 4 * sizeof(T)) && aligned(dst, 4 * sizeof(T));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W,
+                           dH, dW, rows, g.rows_per_block, g.col_blocks, Affine{},
+                           (const int32_t *)nullptr);
+    };
+    if (border == MI_RESIZE_BORDER_MIRROR) {
+        if (pix4) go(linear_generic<T, C, C == 4, kOutSame, false, kBorderMirror>);
+        else go(linear_generic<T, C, false, kOutSame, false, kBorderMirror>);
+    } else {
+        if (pix4) go(linear_generic<T, C, C == 4, kOutSame, false, kBorderWrap>);
+        else go(linear_generic<T, C, false, kOutSame, false, kBorderWrap>);
+    }
+    return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -416,6 +438,31 @@ int resize_linear_roi(const void *src, void *dst, int batch, int H, int W, int C
     case 1: return roi_dispatch<float, 1>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
     case 3: return roi_dispatch<float, 3>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
     default: return roi_dispatch<float, 4>(src, dst, batch, H, W, rois, dst_H, dst_W, st);
+    }
+}
+
+int resize_linear_border(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                         int dst_H, int dst_W, int border, void *stream)
+{
+    const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
+    if (rc != MI_RESIZE_OK) return rc;
+    if (border != MI_RESIZE_BORDER_CLAMP && border != MI_RESIZE_BORDER_MIRROR &&
+        border != MI_RESIZE_BORDER_WRAP)
+        return MI_RESIZE_ERR_PARAM;
+    if (border == MI_RESIZE_BORDER_CLAMP)
+        return resize_linear(src, dst, batch, H, W, C, dtype, dst_H, dst_W, stream);
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == MI_RESIZE_U8) {
+        switch (C) {
+        case 1: return border_dispatch<uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, border, st);
+        case 3: return border_dispatch<uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, border, st);
+        default: return border_dispatch<uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, border, st);
+        }
+    }
+    switch (C) {
+    case 1: return border_dispatch<float, 1>(src, dst, batch, H, W, dst_H, dst_W, border, st);
+    case 3: return border_dispatch<float, 3>(src, dst, batch, H, W, dst_H, dst_W, border, st);
+    default: return border_dispatch<float, 4>(src, dst, batch, H, W, dst_H, dst_W, border, st);
     }
 }
 

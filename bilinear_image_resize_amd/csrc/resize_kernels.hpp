@@ -59,6 +59,49 @@ __device__ __forceinline__ Tap axis_tap(int d, int n_in, int n_out)
     return t;
 }
 
+// Border rules for source coordinates beyond the outermost pixel centres
+// (hnwysp.cn news/129086 s6.1): clamp to the edge (the default), mirror
+// (reflect the coordinate about the outermost pixel centres: x -> -x below 0,
+// x -> 2 (n - 1) - x above n - 1) or wrap (periodic image).  The half-pixel
+// map keeps every coordinate within (-1/2, n - 1/2), so one reflection or one
+// period always brings it inside.  Mirror and wrap act on the exact
+// coordinate before the floor, as the definition states; for linear
+// interpolation mirror equals reflecting the taps about the edge pixel.
+enum : int { kBorderClamp = 0, kBorderMirror = 1, kBorderWrap = 2 };
+
+template <int B>
+__device__ __forceinline__ Tap axis_tap_b(int d, int n_in, int n_out)
+{
+    if constexpr (B == kBorderClamp) {
+        return axis_tap(d, n_in, n_out);
+    } else {
+        long long num = (long long)(2 * d + 1) * n_in - n_out;
+        const int den = 2 * n_out;
+        Tap t;
+        t.den = den;
+        if (n_in == 1) {
+            t.a = t.b = 0;
+            t.r = 0;
+            return t;
+        }
+        const long long last = (long long)(n_in - 1) * den;
+        if constexpr (B == kBorderMirror) {
+            if (num < 0) num = -num;
+            if (num > last) num = 2 * last - num;
+        } else {
+            if (num < 0) num += (long long)n_in * den;
+            if (num >= (long long)n_in * den) num -= (long long)n_in * den;
+        }
+        long long q = (long long)floor((double)num / (double)den);
+        long long r = num - q * den;
+        if (r < 0) { q -= 1; r += den; } else if (r >= den) { q += 1; r -= den; }
+        t.a = (int)q;
+        t.b = (int)(q + 1 < n_in ? q + 1 : (B == kBorderWrap ? 0 : n_in - 1));
+        t.r = (int)r;
+        return t;
+    }
+}
+
 // u rounded half up to 11 fractional bits: floor((4096 r + den) / (2 den)),
 // in [0, 2048].  4096 r + den < 2^31 for den <= 131070.
 __device__ __forceinline__ unsigned weight11(const Tap &t)
@@ -146,7 +189,8 @@ __device__ __forceinline__ Crop load_crop(const int32_t *rois, long long n, int 
 // output pixel per row.  PIX4: C == 4 and the buffers are aligned so that a
 // whole pixel moves as one 4-byte (u8) or 16-byte (f32) access.
 // --------------------------------------------------------------------------
-template <typename T, int C, bool PIX4, int OUT = kOutSame, bool ROI = false>
+template <typename T, int C, bool PIX4, int OUT = kOutSame, bool ROI = false,
+          int BORDER = kBorderClamp>
 __global__ __launch_bounds__(kBlock) void linear_generic(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int col_blocks, Affine aff,
@@ -174,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
     unsigned wx1 = 0;
     float wxf = 0.f;
     auto column = [&]() {
-        const Tap tx = axis_tap(x, crop.w, dW);
+        const Tap tx = axis_tap_b<BORDER>(x, crop.w, dW);
         xa = (crop.x + tx.a) * C;
         xb = (crop.x + tx.b) * C;
         if constexpr (sizeof(T) == 1) wx1 = weight11(tx);
@@ -183,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
     column();
 
     for (; g < g_end; ++g) {
-        const Tap ty = axis_tap(dy, crop.h, dH);
+        const Tap ty = axis_tap_b<BORDER>(dy, crop.h, dH);
         const T *img = src + (size_t)n * img_elems;
         const T *r0 = img + (size_t)(crop.y + ty.a) * row_elems;
         const T *r1 = img + (size_t)(crop.y + ty.b) * row_elems;

@@ -67,11 +67,17 @@
 extern "C" {
 #endif
 
-#define MI_RESIZE_ABI_VERSION 3
+#define MI_RESIZE_ABI_VERSION 4
 
 enum mi_resize_dtype {
     MI_RESIZE_U8 = 0,   /* uint8_t elements  */
     MI_RESIZE_F32 = 1   /* float32 elements  */
+};
+
+enum mi_resize_border {
+    MI_RESIZE_BORDER_CLAMP = 0,   /* clamp to the edge pixel (resize_linear)          */
+    MI_RESIZE_BORDER_MIRROR = 1,  /* reflect about the outermost pixel centres        */
+    MI_RESIZE_BORDER_WRAP = 2     /* periodic image                                   */
 };
 
 enum mi_resize_status {
@@ -136,6 +142,24 @@ int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W
  */
 int resize_linear_roi(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
                       const int32_t *rois, int dst_H, int dst_W, void *stream);
+
+/*
+ * Linear resize with a choice of border rule for source coordinates beyond
+ * the outermost pixel centres (hnwysp.cn news/129086 s6.1: clamp, mirror,
+ * wrap).  The half-pixel map only leaves the image by less than half a pixel,
+ * so the rule decides the second tap of the outermost output pixels of an
+ * enlargement:
+ *   MI_RESIZE_BORDER_CLAMP   x clamped to [0, W-1]: identical to resize_linear;
+ *   MI_RESIZE_BORDER_MIRROR  x reflected about the first / last pixel centre
+ *                            (x -> -x, x -> 2(W-1) - x) before the taps are
+ *                            taken;
+ *   MI_RESIZE_BORDER_WRAP    x taken modulo W (the pixel after the last is the
+ *                            first).
+ * Rows likewise.  Other arguments, layout, weights and errors as
+ * resize_linear; an unknown border returns MI_RESIZE_ERR_PARAM.
+ */
+int resize_linear_border(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                         int dst_H, int dst_W, int border, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *resize_status_string(int status);

@@ -57,9 +57,9 @@ def _load():
         i64 = ctypes.c_int64
         ci = ctypes.c_int
         vp = ctypes.c_void_p
-        for name in ("oracle_linear_u8", "oracle_linear_f32"):
+        for name in ("oracle_linear_u8_border", "oracle_linear_f32_border"):
             f = getattr(lib, name)
-            f.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, i64, i64]
+            f.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, i64, i64, ci]
             f.restype = ci
         lib.oracle_nearest.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, i64, i64]
         lib.oracle_nearest.restype = ci
@@ -86,25 +86,30 @@ def _rows(N, dH, rows):
     return r0, r1
 
 
-def resize_linear(src: np.ndarray, dH: int, dW: int, rows=None) -> np.ndarray:
+BORDERS = {"clamp": 0, "mirror": 1, "wrap": 2}
+
+
+def resize_linear(src: np.ndarray, dH: int, dW: int, rows=None, border: str = "clamp") -> np.ndarray:
     """Linear (bilinear) resize of an NHWC uint8 or float32 array to dH x dW.
 
     ``rows=(r0, r1)`` computes only global output rows r0..r1-1 (row index
     n * dH + dy) and returns them as an array of shape (r1 - r0, dW, C);
-    without it the whole N x dH x dW x C result is returned.
+    without it the whole N x dH x dW x C result is returned.  ``border``
+    ("clamp", "mirror" or "wrap") is the rule for coordinates beyond the
+    outermost pixel centres (hnwysp.cn news/129086 s6.1).
     """
     src = _as_nhwc(src)
     N, H, W, C = src.shape
     r0, r1 = _rows(N, dH, rows)
     lib = _load()
     if src.dtype == np.uint8:
-        fn = lib.oracle_linear_u8
+        fn = lib.oracle_linear_u8_border
     elif src.dtype == np.float32:
-        fn = lib.oracle_linear_f32
+        fn = lib.oracle_linear_f32_border
     else:
         raise TypeError("oracle supports uint8 and float32, got %s" % src.dtype)
     full = np.empty((N * dH, dW, C), dtype=src.dtype)
-    rc = fn(src.ctypes.data, full.ctypes.data, N, H, W, C, dH, dW, r0, r1)
+    rc = fn(src.ctypes.data, full.ctypes.data, N, H, W, C, dH, dW, r0, r1, BORDERS[border])
     if rc != 0:
         raise ValueError("oracle rejected arguments (code %d)" % rc)
     if rows is not None:

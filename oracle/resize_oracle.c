@@ -30,8 +30,11 @@
  *    sizes (W / dW and H / dH), as an exact rational number.
  *  - x is carried as the exact fraction num / den with num = (2 dx + 1) W - dW
  *    and den = 2 dW, so floor and remainder are exact integer operations.
- *  - Border: the coordinate is clamped to [0, size - 1] ([P3] s6.1) and the
- *    second neighbour to size - 1 ([P3] s3.3).
+ *  - Border: by default the coordinate is clamped to [0, size - 1] ([P3] s6.1)
+ *    and the second neighbour to size - 1 ([P3] s3.3).  The *_border entry
+ *    points also take [P3] s6.1's two other rules, mirror (reflection about
+ *    the outermost pixel centres) and wrap (periodic image), applied to the
+ *    exact coordinate.
  *  - uint8: u and v are quantised to 11 fractional bits (2048 = 1.0), rounding
  *    half up; the four products of [P3] s2.2 are formed exactly in integers and
  *    rounded once, half up, at 2^22.  No intermediate rounding.
@@ -60,23 +63,50 @@ static int64_t floor_div(int64_t a, int64_t b)
  * One axis of the coordinate map ([P1] linear sampling; [P3] s2.2, s6.1).
  * Output index d of an axis of out_len samples drawn from in_len samples.
  * The source coordinate x = (d + 1/2) * in_len / out_len - 1/2 equals num/den.
- * After clamping x to [0, in_len - 1]: *i = floor(x), and the fractional part
- * u = x - i is returned as the exact fraction (*u_num) / (*u_den).
+ * A coordinate outside [0, in_len - 1] is brought back by the border rule of
+ * [P3] s6.1:
+ *   BORDER_CLAMP   clamp it to [0, in_len - 1];
+ *   BORDER_MIRROR  reflect it symmetrically about the outermost pixel
+ *                  centres (x -> -x below 0, x -> 2 (in_len - 1) - x above);
+ *   BORDER_WRAP    treat the image as periodic (x -> x + in_len below 0,
+ *                  x -> x - in_len above in_len - 1).
+ * Then *i = floor(x), and the fractional part u = x - i is returned as the
+ * exact fraction (*u_num) / (*u_den).
  */
-static void map_axis(int64_t d, int64_t in_len, int64_t out_len,
-                     int64_t *i, int64_t *u_num, int64_t *u_den)
+enum { BORDER_CLAMP = 0, BORDER_MIRROR = 1, BORDER_WRAP = 2 };
+
+static void map_axis_border(int64_t d, int64_t in_len, int64_t out_len, int border,
+                            int64_t *i, int64_t *u_num, int64_t *u_den)
 {
     int64_t num = (2 * d + 1) * in_len - out_len;
     int64_t den = 2 * out_len;
     *u_den = den;
+    if (in_len == 1) {                  /* a single pixel: every rule gives it */
+        *i = 0;
+        *u_num = 0;
+        return;
+    }
+    if (border == BORDER_MIRROR) {
+        if (num < 0)
+            num = -num;
+        if (num > (in_len - 1) * den)
+            num = 2 * (in_len - 1) * den - num;
+    } else if (border == BORDER_WRAP) {
+        if (num < 0)
+            num += in_len * den;
+        if (num >= in_len * den)
+            num -= in_len * den;
+    }
     if (num < 0) {                      /* x < 0: clamp to 0 */
         *i = 0;
         *u_num = 0;
         return;
     }
-    if (num > (in_len - 1) * den) {     /* x > in_len - 1: clamp */
-        *i = in_len - 1;
-        *u_num = 0;
+    if (num > (in_len - 1) * den) {     /* x > in_len - 1: clamp (clamp rule, */
+        *i = in_len - 1;                /* or the wrap rule's last interval  */
+        *u_num = num - (in_len - 1) * den;   /* handled below)              */
+        if (border != BORDER_WRAP)
+            *u_num = 0;
         return;
     }
     *i = floor_div(num, den);
@@ -89,31 +119,42 @@ static int64_t next_index(int64_t i, int64_t len)
     return (i + 1 < len) ? (i + 1) : (len - 1);
 }
 
+/* Second neighbour under a border rule: under wrap the pixel after the last
+ * is the first (periodic image); otherwise as next_index. */
+static int64_t next_index_border(int64_t i, int64_t len, int border)
+{
+    if (border == BORDER_WRAP)
+        return (i + 1 < len) ? (i + 1) : 0;
+    return next_index(i, len);
+}
+
 /* u quantised to 11 fractional bits: round-half-up of 2048 * u_num / u_den. */
 static int64_t quantise_11(int64_t u_num, int64_t u_den)
 {
     return floor_div(4096 * u_num + u_den, 2 * u_den);
 }
 
-int oracle_linear_u8(const uint8_t *src, uint8_t *dst,
-                     int N, int H, int W, int C, int dH, int dW,
-                     int64_t row_begin, int64_t row_end)
+int oracle_linear_u8_border(const uint8_t *src, uint8_t *dst,
+                            int N, int H, int W, int C, int dH, int dW,
+                            int64_t row_begin, int64_t row_end, int border)
 {
     if (!src || !dst || N < 1 || H < 1 || W < 1 || C < 1 || dH < 1 || dW < 1)
         return 1;
+    if (border < BORDER_CLAMP || border > BORDER_WRAP)
+        return 3;
     if (row_begin < 0 || row_end > (int64_t)N * dH || row_begin > row_end)
         return 2;
     for (int64_t r = row_begin; r < row_end; ++r) {
         int64_t n = r / dH, y = r % dH;
         int64_t j, v_num, v_den;
-        map_axis(y, H, dH, &j, &v_num, &v_den);
-        int64_t j1 = next_index(j, H);
+        map_axis_border(y, H, dH, border, &j, &v_num, &v_den);
+        int64_t j1 = next_index_border(j, H, border);
         int64_t V = quantise_11(v_num, v_den);           /* v * 2048 */
         const uint8_t *img = src + (size_t)n * H * W * C;
         for (int64_t x = 0; x < dW; ++x) {
             int64_t i, u_num, u_den;
-            map_axis(x, W, dW, &i, &u_num, &u_den);
-            int64_t i1 = next_index(i, W);
+            map_axis_border(x, W, dW, border, &i, &u_num, &u_den);
+            int64_t i1 = next_index_border(i, W, border);
             int64_t U = quantise_11(u_num, u_den);       /* u * 2048 */
             for (int64_t c = 0; c < C; ++c) {
                 /* src(i, j): column i, row j */
@@ -134,25 +175,27 @@ int oracle_linear_u8(const uint8_t *src, uint8_t *dst,
     return 0;
 }
 
-int oracle_linear_f32(const float *src, float *dst,
-                      int N, int H, int W, int C, int dH, int dW,
-                      int64_t row_begin, int64_t row_end)
+int oracle_linear_f32_border(const float *src, float *dst,
+                             int N, int H, int W, int C, int dH, int dW,
+                             int64_t row_begin, int64_t row_end, int border)
 {
     if (!src || !dst || N < 1 || H < 1 || W < 1 || C < 1 || dH < 1 || dW < 1)
         return 1;
+    if (border < BORDER_CLAMP || border > BORDER_WRAP)
+        return 3;
     if (row_begin < 0 || row_end > (int64_t)N * dH || row_begin > row_end)
         return 2;
     for (int64_t r = row_begin; r < row_end; ++r) {
         int64_t n = r / dH, y = r % dH;
         int64_t j, v_num, v_den;
-        map_axis(y, H, dH, &j, &v_num, &v_den);
-        int64_t j1 = next_index(j, H);
+        map_axis_border(y, H, dH, border, &j, &v_num, &v_den);
+        int64_t j1 = next_index_border(j, H, border);
         double v = (double)v_num / (double)v_den;
         const float *img = src + (size_t)n * H * W * C;
         for (int64_t x = 0; x < dW; ++x) {
             int64_t i, u_num, u_den;
-            map_axis(x, W, dW, &i, &u_num, &u_den);
-            int64_t i1 = next_index(i, W);
+            map_axis_border(x, W, dW, border, &i, &u_num, &u_den);
+            int64_t i1 = next_index_border(i, W, border);
             double u = (double)u_num / (double)u_den;
             for (int64_t c = 0; c < C; ++c) {
                 double s_ij   = img[((size_t)j  * W + i ) * C + c];
@@ -168,6 +211,20 @@ int oracle_linear_f32(const float *src, float *dst,
         }
     }
     return 0;
+}
+
+int oracle_linear_u8(const uint8_t *src, uint8_t *dst, int N, int H, int W, int C,
+                     int dH, int dW, int64_t row_begin, int64_t row_end)
+{
+    return oracle_linear_u8_border(src, dst, N, H, W, C, dH, dW, row_begin, row_end,
+                                   BORDER_CLAMP);
+}
+
+int oracle_linear_f32(const float *src, float *dst, int N, int H, int W, int C,
+                      int dH, int dW, int64_t row_begin, int64_t row_end)
+{
+    return oracle_linear_f32_border(src, dst, N, H, W, C, dH, dW, row_begin, row_end,
+                                    BORDER_CLAMP);
 }
 
 /*

@@ -448,3 +448,22 @@ def test_roi_random(dtype, path, monkeypatch):
         say("case roi %s %s #%d %s" % (dtype, path, i, (N, H, W, C, dH, dW)))
         assert_parity(run_roi(s, rois, dH, dW), oracle.resize_linear_roi(s, rois, dH, dW),
                       "roi #%d" % i)
+
+
+# --------------------------------------------------------------------------
+# border rules (mirror, wrap)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("border", ["mirror", "wrap"])
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_border_modes(border, dtype):
+    r = np.random.default_rng(717 + (dtype == "f32") + 2 * (border == "wrap"))
+    shapes = [random_case(r) for _ in range(40)] + EDGE[:14] + [(1, 3, 3, 1, 6144, 6144 // 2048 * 3)]
+    for i, (N, H, W, C, dH, dW) in enumerate(shapes):
+        say("case border %s %s #%d %s" % (border, dtype, i, (N, H, W, C, dH, dW)))
+        s = random_image(r, (N, H, W, C), dtype)
+        src = torch.from_numpy(s).cuda()
+        dst = torch.empty((N, dH, dW, C), dtype=src.dtype, device="cuda")
+        R.resize_linear_border(src, dst, border=border)
+        torch.cuda.synchronize()
+        assert_parity(dst.cpu().numpy(), oracle.resize_linear(s, dH, dW, border=border),
+                      "border %s #%d %s" % (border, i, (N, H, W, C, dH, dW)))

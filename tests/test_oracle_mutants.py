@@ -32,6 +32,10 @@ MUTANTS = {
     "f32_dropped_term": ("+ u * v * s_i1j1;", ";"),
     "f32_same_row": ("double v = (double)v_num / (double)v_den;",
                      "double v = (double)v_num / (double)v_den; j1 = j;"),
+    "mirror_about_edge": ("            num = 2 * (in_len - 1) * den - num;",
+                          "            num = 2 * (in_len - 1) * den - num - den;"),
+    "wrap_neighbour_clamped": ("        return (i + 1 < len) ? (i + 1) : 0;",
+                               "        return (i + 1 < len) ? (i + 1) : (len - 1);"),
 }
 # (truncating instead of flooring the division is an equivalent mutant: the
 # coordinate is clamped to be non-negative before it is divided.)

@@ -413,3 +413,43 @@ def test_roi_full_image_is_plain_resize():
     s = rand_img(r, (3, 17, 23, 3), np.uint8)
     full = [(0, 0, 23, 17)] * 3
     assert np.array_equal(oracle.resize_linear_roi(s, full, 9, 31), oracle.resize_linear(s, 9, 31))
+
+
+# --------------------------------------------------------------------------
+# border rules: wrap = the centre tile of the clamp resize of the image tiled
+# 3 x 3 (same scale, coordinates shifted by one image); mirror = the centre of
+# the clamp resize of the image padded by reflection about its edge pixels
+# (numpy's "reflect" padding).  In both, the centre never reaches the padded
+# image's own border, so the (pinned) clamp resize decides it.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [np.uint8, np.float32])
+def test_border_wrap_and_mirror_by_extension(dtype):
+    r = rng(21)
+    for _ in range(25):
+        H, W = (int(v) for v in r.integers(2, 14, size=2))
+        dH, dW = (int(v) for v in r.integers(1, 40, size=2))
+        s = rand_img(r, (1, H, W, 2), dtype)
+        # uint8: bit-exact (same integer weights); float32: the two evaluate
+        # the same weighted sum in a different order before one rounding
+        tol = 0 if dtype == np.uint8 else 1.2e-7
+        tiled = np.tile(s, (1, 3, 3, 1))
+        big = oracle.resize_linear(tiled, 3 * dH, 3 * dW)
+        got = oracle.resize_linear(s, dH, dW, border="wrap")
+        assert np.max(np.abs(got.astype(np.float64) - big[:, dH:2 * dH, dW:2 * dW])) <= tol
+        padded = np.pad(s, ((0, 0), (H, H), (W, W), (0, 0)), mode="reflect")
+        big = oracle.resize_linear(np.ascontiguousarray(padded), 3 * dH, 3 * dW)
+        got = oracle.resize_linear(s, dH, dW, border="mirror")
+        assert np.max(np.abs(got.astype(np.float64) - big[:, dH:2 * dH, dW:2 * dW])) <= tol
+
+
+def test_border_rules_agree_inside():
+    """Downscales by 2 never leave the image: all three rules agree; an
+    enlargement differs only in the outermost output pixels."""
+    r = rng(22)
+    s = rand_img(r, (1, 16, 20, 3), np.uint8)
+    for b in ("mirror", "wrap"):
+        assert np.array_equal(oracle.resize_linear(s, 8, 10, border=b), oracle.resize_linear(s, 8, 10))
+        up = oracle.resize_linear(s, 64, 80, border=b)
+        ref = oracle.resize_linear(s, 64, 80)
+        assert np.array_equal(up[:, 2:-2, 2:-2], ref[:, 2:-2, 2:-2])
+        assert not np.array_equal(up, ref)
