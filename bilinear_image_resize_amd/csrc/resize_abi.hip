@@ -49,6 +49,7 @@ int check_args(const void *src, const void *dst, int batch, int H, int W, int C,
     if (batch < 1 || H < 1 || W < 1 || dH < 1 || dW < 1) return MI_RESIZE_ERR_SHAPE;
     if (H > kMaxDim || W > kMaxDim || dH > kMaxDim || dW > kMaxDim) return MI_RESIZE_ERR_SHAPE;
     if ((long long)batch * dH * dW > kMaxOutPixels) return MI_RESIZE_ERR_SHAPE;
+    if ((long long)batch * H * W > kMaxOutPixels) return MI_RESIZE_ERR_SHAPE;
     const size_t es = dtype == MI_RESIZE_U8 ? 1 : 4;
     const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
     const uintptr_t s1 = s0 + (size_t)batch * H * W * C * es;
@@ -77,9 +78,19 @@ Grid band_grid(long long rows_total, int dW)
     return g;
 }
 
-int launched()
+// Launch `kernel` through hipLaunchKernel, which returns this launch's own
+// status (an earlier error elsewhere on the thread cannot leak into it).  The
+// arguments are converted to the kernel's exact parameter types before their
+// addresses are handed over.
+template <typename T> struct same { using type = T; };
+
+template <typename... P>
+int launch(void (*kernel)(P...), dim3 grid, dim3 block, unsigned lds_bytes, hipStream_t st,
+           typename same<P>::type... args)
 {
-    return hipGetLastError() == hipSuccess ? MI_RESIZE_OK : MI_RESIZE_ERR_HIP;
+    void *argv[] = {(void *)&args..., nullptr};
+    const hipError_t e = hipLaunchKernel((const void *)kernel, grid, block, argv, lds_bytes, st);
+    return e == hipSuccess ? MI_RESIZE_OK : MI_RESIZE_ERR_HIP;
 }
 
 template <typename T, int C, int OUT = kOutSame, bool ROI = false>
@@ -91,16 +102,12 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
     const Grid g = band_grid(rows, dW);
     const bool pix4 = OUT == kOutSame && C == 4 && aligned(src, 4 * sizeof(T)) &&
                       aligned(dst, 4 * sizeof(T));
-    if (pix4) {
-        hipLaunchKernelGGL((linear_generic<T, C, C == 4 && OUT == kOutSame, OUT, ROI>),
-                           dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W, dH, dW,
-                           rows, g.rows_per_block, g.col_blocks, aff, rois);
-    } else {
-        hipLaunchKernelGGL((linear_generic<T, C, false, OUT, ROI>), dim3(g.blocks), dim3(kBlock),
-                           0, st, (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block,
-                           g.col_blocks, aff, rois);
-    }
-    return launched();
+    auto go = [&](auto kernel) {
+        return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W, dH,
+                      dW, rows, g.rows_per_block, g.col_blocks, aff, rois);
+    };
+    if (pix4) return go(linear_generic<T, C, C == 4 && OUT == kOutSame, OUT, ROI>);
+    return go(linear_generic<T, C, false, OUT, ROI>);
 }
 
 constexpr long long kMaxGridY = 65535;
@@ -111,9 +118,8 @@ int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStr
     constexpr int seg = kHalfLanes * HalfShape<C>::PX;
     const long long rows = (long long)batch * dH;
     const dim3 grid((dW + seg - 1) / seg, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
-    hipLaunchKernelGGL((linear_half_u8<C>), grid, dim3(kHalfLanes), 0, st, (const uint8_t *)src,
-                       (uint8_t *)dst, dW, rows);
-    return launched();
+    return launch(linear_half_u8<C>, grid, dim3(kHalfLanes), 0, st, (const uint8_t *)src,
+                  (uint8_t *)dst, dW, rows);
 }
 
 // Exact 2:1 uint8 downscale whose rows split into whole 16-byte chunks and
@@ -175,15 +181,14 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8
     const int per_lane = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src,
-                           dst, H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
-                           (long long)batch * H * W * C, aff, rois);
+        return launch(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src, dst,
+                      H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
+                      (long long)batch * H * W * C, aff, rois);
     };
-    if (per_lane <= 1) go(rowseg<T, C, NEAREST, 1, OUT, ROI>);
-    else if (per_lane <= 2) go(rowseg<T, C, NEAREST, 2, OUT, ROI>);
-    else if (per_lane <= 4) go(rowseg<T, C, NEAREST, 4, OUT, ROI>);
-    else go(rowseg<T, C, NEAREST, 8, OUT, ROI>);
-    rc = launched();
+    if (per_lane <= 1) rc = go(rowseg<T, C, NEAREST, 1, OUT, ROI>);
+    else if (per_lane <= 2) rc = go(rowseg<T, C, NEAREST, 2, OUT, ROI>);
+    else if (per_lane <= 4) rc = go(rowseg<T, C, NEAREST, 4, OUT, ROI>);
+    else rc = go(rowseg<T, C, NEAREST, 8, OUT, ROI>);
     return true;
 }
 
@@ -194,12 +199,11 @@ int launch_up2_u8(const void *src, void *dst, int batch, int H, int W, hipStream
     const long long rows = (long long)batch * H;
     const dim3 grid((chunks_per_row + 63) / 64, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
     if constexpr (NEAREST)
-        hipLaunchKernelGGL((nearest_up2_u8<C>), grid, dim3(64), 0, st, (const uint8_t *)src,
-                           (uint8_t *)dst, H, W, rows, chunks_per_row);
+        return launch(nearest_up2_u8<C>, grid, dim3(64), 0, st, (const uint8_t *)src,
+                      (uint8_t *)dst, H, W, rows, chunks_per_row);
     else
-        hipLaunchKernelGGL((linear_up2_u8<C>), grid, dim3(64), 0, st, (const uint8_t *)src,
-                           (uint8_t *)dst, H, W, rows, chunks_per_row);
-    return launched();
+        return launch(linear_up2_u8<C>, grid, dim3(64), 0, st, (const uint8_t *)src,
+                      (uint8_t *)dst, H, W, rows, chunks_per_row);
 }
 
 // Exact 2x uint8 upscale whose rows split into whole, 16-byte aligned lanes.
@@ -218,17 +222,16 @@ int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, 
     const long long rows = (long long)batch * dH;
     const Grid g = band_grid(rows, dW);
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const uint8_t *)src,
-                           (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks);
+        return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const uint8_t *)src,
+                      (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks);
     };
     if constexpr (BPP % 16 == 0) {
-        if (aligned(src, 16) && aligned(dst, 16)) { go(nearest_generic<BPP, 16>); return launched(); }
+        if (aligned(src, 16) && aligned(dst, 16)) return go(nearest_generic<BPP, 16>);
     }
     if constexpr (BPP % 4 == 0) {
-        if (aligned(src, 4) && aligned(dst, 4)) { go(nearest_generic<BPP, 4>); return launched(); }
+        if (aligned(src, 4) && aligned(dst, 4)) return go(nearest_generic<BPP, 4>);
     }
-    go(nearest_generic<BPP, 1>);
-    return launched();
+    return go(nearest_generic<BPP, 1>);
 }
 
 template <typename T, int C>
@@ -301,18 +304,16 @@ int border_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
     const Grid g = band_grid(rows, dW);
     const bool pix4 = C == 4 && aligned(src, 4 * sizeof(T)) && aligned(dst, 4 * sizeof(T));
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W,
-                           dH, dW, rows, g.rows_per_block, g.col_blocks, Affine{},
-                           (const int32_t *)nullptr);
+        return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W, dH,
+                      dW, rows, g.rows_per_block, g.col_blocks, Affine{},
+                      (const int32_t *)nullptr);
     };
     if (border == MI_RESIZE_BORDER_MIRROR) {
-        if (pix4) go(linear_generic<T, C, C == 4, kOutSame, false, kBorderMirror>);
-        else go(linear_generic<T, C, false, kOutSame, false, kBorderMirror>);
-    } else {
-        if (pix4) go(linear_generic<T, C, C == 4, kOutSame, false, kBorderWrap>);
-        else go(linear_generic<T, C, false, kOutSame, false, kBorderWrap>);
+        if (pix4) return go(linear_generic<T, C, C == 4, kOutSame, false, kBorderMirror>);
+        return go(linear_generic<T, C, false, kOutSame, false, kBorderMirror>);
     }
-    return launched();
+    if (pix4) return go(linear_generic<T, C, C == 4, kOutSame, false, kBorderWrap>);
+    return go(linear_generic<T, C, false, kOutSame, false, kBorderWrap>);
 }
 
 }  // namespace
@@ -328,7 +329,7 @@ const char *resize_status_string(int status)
     case MI_RESIZE_ERR_NULL: return "src or dst is a null pointer";
     case MI_RESIZE_ERR_SHAPE:
         return "a size is out of range (need 1 <= H, W, dst_H, dst_W <= 65535, batch >= 1, "
-               "batch*dst_H*dst_W <= 2^40)";
+               "batch*H*W and batch*dst_H*dst_W <= 2^40)";
     case MI_RESIZE_ERR_CHANNELS: return "channel count must be 1, 3 or 4";
     case MI_RESIZE_ERR_DTYPE: return "dtype must be MI_RESIZE_U8 (0) or MI_RESIZE_F32 (1)";
     case MI_RESIZE_ERR_OVERLAP: return "src and dst buffers overlap";
@@ -481,8 +482,9 @@ int resize_copy_bytes(const void *src, void *dst, int64_t nbytes, void *stream)
         if (n16 > 0) {
             long long blocks = (n16 + kBlock - 1) / kBlock;
             if (blocks > 256 * 32) blocks = 256 * 32;
-            hipLaunchKernelGGL(copy_16, dim3((unsigned)blocks), dim3(kBlock), 0, st,
-                               (const uint4 *)src, (uint4 *)dst, n16);
+            const int rc = launch(copy_16, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                                  (const uint4 *)src, (uint4 *)dst, n16);
+            if (rc != MI_RESIZE_OK) return rc;
             head = n16 * 16;
         }
     }
@@ -490,10 +492,10 @@ int resize_copy_bytes(const void *src, void *dst, int64_t nbytes, void *stream)
     if (rest > 0) {
         long long blocks = (rest + kBlock - 1) / kBlock;
         if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
-        hipLaunchKernelGGL(copy_1, dim3((unsigned)blocks), dim3(kBlock), 0, st,
-                           (const uint8_t *)src + head, (uint8_t *)dst + head, rest);
+        return launch(copy_1, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                      (const uint8_t *)src + head, (uint8_t *)dst + head, rest);
     }
-    return launched();
+    return MI_RESIZE_OK;
 }
 
 }  // extern "C"

@@ -56,7 +56,7 @@
  * runtime at the caller's next synchronisation.
  *
  * Limits: 1 <= H, W, dst_H, dst_W <= 65535; batch >= 1;
- * batch * dst_H * dst_W <= 2^40.
+ * batch * H * W <= 2^40 and batch * dst_H * dst_W <= 2^40.
  */
 #ifndef MI_RESIZE_H
 #define MI_RESIZE_H

@@ -56,7 +56,8 @@ def test_argument_validation(name):
     assert call(name, src=None) == 1
     assert call(name, dst=None) == 1
     for kw in ({"batch": 0}, {"H": 0}, {"W": -1}, {"dH": 0}, {"dW": 0},
-               {"H": 65536}, {"dW": 70000}, {"batch": 1 << 30, "dH": 65535, "dW": 65535}):
+               {"H": 65536}, {"dW": 70000}, {"batch": 1 << 30, "dH": 65535, "dW": 65535},
+               {"batch": 1 << 30, "H": 40000, "W": 40000, "dH": 1, "dW": 1}):
         assert call(name, **kw) == 2, kw
     for c in (0, 2, 5, 16):
         assert call(name, C=c) == 3
