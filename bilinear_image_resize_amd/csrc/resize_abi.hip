@@ -178,8 +178,12 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     SegPlan pl;
     // a crop is at most W wide, so the whole-image bound covers every crop
     if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, pl)) return false;
-    // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8
-    const int per_lane = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
+    // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8;
+    // a slot then holds 64 lanes x that many chunks (the kernel writes its
+    // clamped spare chunks there instead of branching around them)
+    const int need = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
+    const int per_lane = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+    pl.seg_cap = per_lane * kSegLanes * 16;
     auto go = [&](auto kernel) {
         return launch(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src, dst,
                       H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,

@@ -608,15 +608,16 @@ constexpr int kSegReadSlack = 16;  // bytes a two-tap LDS read may run past the 
 
 // One source-row segment to stage: `bytes` bytes from p (uniform across the
 // wave) into an LDS slot, as 16-byte chunks from the 16-byte boundary at or
-// below p.  Chunks [k_lo, k_hi) lie wholly inside the source buffer and are
-// loaded as one 16-byte access each; the rest (only at the very start or end
-// of the buffer) are copied byte by byte, so nothing outside is read.
+// below p.  `clean` says every chunk lies wholly inside the source buffer
+// [lo, hi), which is the case for every row except possibly the buffer's
+// first and last ones.
 struct Segment {
     const uint8_t *base;   // 16-byte aligned address of chunk 0
     uint8_t *slot;
     int mis;               // offset of p inside the slot
-    int n16, k_lo, k_hi;
-    bool on;
+    int n16;               // chunks to stage
+    bool on;               // this row needs staging
+    bool clean;
     __device__ void plan(bool want, uint8_t *slot_, const uint8_t *p, int bytes,
                          const uint8_t *lo, const uint8_t *hi)
     {
@@ -625,51 +626,69 @@ struct Segment {
         mis = (int)((uintptr_t)p & 15);
         base = p - mis;
         n16 = (mis + bytes + 15) >> 4;
-        const long long first = base >= lo ? 0 : (long long)((lo - base + 15) >> 4);
-        const long long last = (long long)((hi - base) >> 4);   // chunks [0, last) end at or before hi
-        k_lo = (int)(first < n16 ? first : n16);
-        k_hi = (int)(last < n16 ? (last > k_lo ? last : k_lo) : n16);
-    }
-    __device__ void write_edge(int k, const uint8_t *lo, const uint8_t *hi) const
-    {
-        const uint8_t *q = base + 16 * k;
-        uint8_t t[16];
-#pragma unroll
-        for (int b = 0; b < 16; ++b) t[b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
-        uint4 v;
-        __builtin_memcpy(&v, t, 16);
-        *(uint4 *)(slot + 16 * k) = v;
+        clean = base >= lo && base + 16 * (size_t)n16 <= hi;
     }
 };
 
+// Staging of a segment that touches the start or end of the source buffer:
+// chunks wholly inside are copied as 16 bytes, the others byte by byte, so
+// nothing outside [lo, hi) is read.  Rare (at most the buffer's first and
+// last rows), so its loops stay rolled: it sits behind a wave-uniform branch
+// and costs nothing when not taken.
+__device__ __forceinline__ void stage_edge_segment(const Segment &S, const uint8_t *lo,
+                                                   const uint8_t *hi)
+{
+#pragma unroll 1
+    for (int k = threadIdx.x; k < S.n16; k += kSegLanes) {
+        const uint8_t *q = S.base + 16 * k;
+        if (q >= lo && q + 16 <= hi) {
+            *(uint4 *)(S.slot + 16 * k) = *(const uint4 *)q;
+        } else {
+#pragma unroll 1
+            for (int b = 0; b < 16; ++b)
+                S.slot[16 * k + b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
+        }
+    }
+}
+
 // Stage up to two segments with every global load of the lane issued before
 // any LDS write, so the wave waits for memory once per output row, not once
-// per chunk.  KMAX bounds the chunks per lane per segment (n16 <= 64 KMAX).
+// per chunk.  A lane handles chunks lane, lane + 64, ... (KMAX of them);
+// a lane past the segment re-reads its last chunk and writes into the slot's
+// slack (a slot holds 64 KMAX chunks), so the clean case has no divergent
+// branches at all.
 template <int KMAX>
 __device__ __forceinline__ void stage_pair(const Segment &A, const Segment &B,
                                            const uint8_t *lo, const uint8_t *hi)
 {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x;
+    const bool a_fast = A.on && A.clean, b_fast = B.on && B.clean;
     v4u va[KMAX], vb[KMAX];
+    if (a_fast) {
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-        const int k = lane + kSegLanes * i;
-        va[i] = (A.on && k >= A.k_lo && k < A.k_hi) ? *(const v4u *)(A.base + 16 * k) : v4u{0, 0, 0, 0};
-        vb[i] = (B.on && k >= B.k_lo && k < B.k_hi) ? *(const v4u *)(B.base + 16 * k) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-        const int k = lane + kSegLanes * i;
-        if (A.on && k < A.n16) {
-            if (k >= A.k_lo && k < A.k_hi) *(v4u *)(A.slot + 16 * k) = va[i];
-            else A.write_edge(k, lo, hi);
-        }
-        if (B.on && k < B.n16) {
-            if (k >= B.k_lo && k < B.k_hi) *(v4u *)(B.slot + 16 * k) = vb[i];
-            else B.write_edge(k, lo, hi);
+        for (int i = 0; i < KMAX; ++i) {
+            const int k = min(lane + kSegLanes * i, A.n16 - 1);
+            va[i] = *(const v4u *)(A.base + 16 * k);
         }
     }
+    if (b_fast) {
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+            const int k = min(lane + kSegLanes * i, B.n16 - 1);
+            vb[i] = *(const v4u *)(B.base + 16 * k);
+        }
+    }
+    if (a_fast) {
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) *(v4u *)(A.slot + 16 * (lane + kSegLanes * i)) = va[i];
+    }
+    if (b_fast) {
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) *(v4u *)(B.slot + 16 * (lane + kSegLanes * i)) = vb[i];
+    }
+    if (A.on && !A.clean) stage_edge_segment(A, lo, hi);
+    if (B.on && !B.clean) stage_edge_segment(B, lo, hi);
 }
 
 // Store N elements of one lane: vectorised when the chunk is whole and
@@ -701,18 +720,21 @@ __device__ __forceinline__ void store_chunk(T *out, const T (&v)[N], int valid)
 
 // Row map that steps from output row to output row without dividing.
 struct RowStepper {
-    long long q, r;        // floor and remainder of num / den for the current row
-    long long dq, dr;      // 2 n_in = dq * den + dr
-    long long den;
+    // all below 2^18: q in [-1, n_in], r < den = 2 n_out <= 131070
+    int q, r;              // floor and remainder of num / den for the current row
+    int dq, dr;            // 2 n_in = dq * den + dr
+    int den;
     __device__ void init(int d, int n_in, int n_out)
     {
-        den = 2LL * n_out;
+        den = 2 * n_out;
         const long long num = (long long)(2 * d + 1) * n_in - n_out;
-        q = (long long)floor((double)num / (double)den);
-        r = num - q * den;
-        if (r < 0) { q -= 1; r += den; } else if (r >= den) { q += 1; r -= den; }
-        dq = (2LL * n_in) / den;
-        dr = (2LL * n_in) - dq * den;
+        long long q64 = (long long)floor((double)num / (double)den);
+        long long r64 = num - q64 * den;
+        if (r64 < 0) { q64 -= 1; r64 += den; } else if (r64 >= den) { q64 += 1; r64 -= den; }
+        q = (int)q64;
+        r = (int)r64;
+        dq = (2 * n_in) / den;
+        dr = 2 * n_in - dq * den;
     }
     __device__ void next()
     {
