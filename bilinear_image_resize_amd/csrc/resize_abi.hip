@@ -8,6 +8,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "resize_kernels.hpp"
 
 namespace {
@@ -131,13 +133,18 @@ bool half_path_fits(int C, int H, int W, int dH, int dW, const void *src, const 
     return dW % q == 0;
 }
 
-// LDS bytes one row-segment workgroup may use (two slots).  Beyond it the
+// LDS bytes one row-segment wave may use (its two slots).  Beyond it the
 // segment is too wide (strong downscale) and the direct kernels run instead;
-// at 16 KiB a CU still holds 10 such one-wave workgroups, and a slot of at
+// a workgroup of kSegWaves such waves then takes 64 KiB, and a slot of at
 // most 8 KiB is at most 8 16-byte chunks per lane.
 constexpr int kSegLdsBudget = 16 * 1024;
-// One-wave workgroups a row-segment launch aims for: 32 per CU on 256 CUs.
-constexpr long long kSegTargetBlocks = 8192;
+// Row bands (one wave each) a row-segment launch aims for: 256 per CU on
+// 256 CUs, but at least kSegMinBandRows rows each.  Short bands keep many
+// independent waves in flight and balance the tail; a band's set-up (its
+// column table, in fp64) is paid once per band, so single-row bands cost
+// more than they gain.
+constexpr long long kSegTargetBands = 65536;
+constexpr long long kSegMinBandRows = 2;
 // Below this many output pixels the launch is latency-bound and the direct
 // kernels (no staging round trip, no per-lane column table of PX entries)
 // finish first.
@@ -162,10 +169,11 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, SegPlan
     if (2 * cap > kSegLdsBudget) return false;
     pl.seg_cap = (int)cap;
     const long long gx = (dW + cols - 1) / cols;
-    long long rpb = (rows * gx + kSegTargetBlocks - 1) / kSegTargetBlocks;
-    if (rpb < 1) rpb = 1;
+    long long rpb = (rows * gx + kSegTargetBands - 1) / kSegTargetBands;
+    if (rpb < kSegMinBandRows) rpb = kSegMinBandRows;
     pl.rows_per_block = (int)rpb;
-    pl.grid = dim3((unsigned)gx, (unsigned)((rows + rpb - 1) / rpb));
+    const long long bands = (rows + rpb - 1) / rpb;
+    pl.grid = dim3((unsigned)gx, (unsigned)((bands + kSegWaves - 1) / kSegWaves));
     return true;
 }
 
@@ -185,14 +193,31 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const int per_lane = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
     pl.seg_cap = per_lane * kSegLanes * 16;
     auto go = [&](auto kernel) {
-        return launch(kernel, pl.grid, dim3(kSegLanes), 2 * pl.seg_cap, st, (const T *)src, dst,
+        return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), kSegWaves * 2 * pl.seg_cap, st,
+                      (const T *)src, dst,
                       H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
                       (long long)batch * H * W * C, aff, rois);
     };
-    if (per_lane <= 1) rc = go(rowseg<T, C, NEAREST, 1, OUT, ROI>);
-    else if (per_lane <= 2) rc = go(rowseg<T, C, NEAREST, 2, OUT, ROI>);
-    else if (per_lane <= 4) rc = go(rowseg<T, C, NEAREST, 4, OUT, ROI>);
-    else rc = go(rowseg<T, C, NEAREST, 8, OUT, ROI>);
+    // Non-temporal staging loads when no source row is used by two output
+    // rows (a row step of at least 2 for linear, 1 for nearest): nothing
+    // staged is read again, so the loads need not allocate in the caches.
+    // Where rows are shared, a neighbouring band re-reads its boundary rows
+    // from L2, and crops can upscale, so those keep cached loads.
+    const bool stream = NEAREST ? H >= dH : H >= 2 * dH;
+    auto pick = [&](auto nt) {
+        constexpr bool NT = decltype(nt)::value;
+        if (per_lane <= 1) return go(rowseg<T, C, NEAREST, 1, NT, OUT, ROI>);
+        if (per_lane <= 2) return go(rowseg<T, C, NEAREST, 2, NT, OUT, ROI>);
+        if (per_lane <= 4) return go(rowseg<T, C, NEAREST, 4, NT, OUT, ROI>);
+        return go(rowseg<T, C, NEAREST, 8, NT, OUT, ROI>);
+    };
+    if constexpr (!ROI) {
+        if (stream) {
+            rc = pick(std::true_type{});
+            return true;
+        }
+    }
+    rc = pick(std::false_type{});
     return true;
 }
 

@@ -572,10 +572,12 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
 // --------------------------------------------------------------------------
 // Row-segment kernel: any scale, linear or nearest, u8 or f32, C in {1,3,4}.
 //
-// A workgroup is one wave (64 lanes).  It owns a segment of 64 * PX
-// consecutive output columns and a band of `rows_per_block` consecutive
-// output rows.  Each lane owns PX consecutive output pixels of the segment
-// and keeps their column taps and weights in registers for the whole band.
+// A wave (64 lanes) owns a segment of 64 * PX consecutive output columns
+// and a band of `rows_per_block` consecutive output rows; a workgroup packs
+// kSegWaves such waves, each on its own band with its own LDS slots, so no
+// workgroup-wide barrier is needed.  Each lane owns PX consecutive output
+// pixels of the segment and keeps their column taps and weights in
+// registers for the whole band.
 //
 // Per output row the wave stages the source row(s) it needs - only the
 // columns [sa, sb] its segment touches - into LDS with 16-byte loads that
@@ -586,6 +588,10 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
 // one unaligned LDS read fetches them together.  Two LDS slots cache the
 // last two staged source rows, so consecutive output rows that share a
 // source row (every upscale) stage it once.
+//
+// The staging is pipelined one row deep (see issue_segment), and rows that
+// no other output row needs are loaded and the results stored with
+// non-temporal hints.
 //
 // Row taps advance incrementally from row to row: the numerator of the
 // source coordinate grows by 2H per output row, so the quotient and
@@ -605,6 +611,22 @@ template <> struct SegShape<float, 4> { static constexpr int PX = 1; };
 
 constexpr int kSegLanes = 64;
 constexpr int kSegReadSlack = 16;  // bytes a two-tap LDS read may run past the segment
+// Waves per row-segment workgroup.  Each wave works alone on a band of its
+// own, with its own two LDS slots; packing several into one workgroup keeps
+// the CU's workgroup slots from capping how many waves it holds.
+constexpr int kSegWaves = 4;
+
+__device__ __forceinline__ int seg_lane() { return (int)threadIdx.x & (kSegLanes - 1); }
+
+// Orders this wave's LDS accesses before and after it.  A wave's LDS
+// operations complete in issue order, so keeping the compiler from moving
+// them across this point is all the synchronisation a wave-private slot needs.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // One source-row segment to stage: `bytes` bytes from p (uniform across the
 // wave) into an LDS slot, as 16-byte chunks from the 16-byte boundary at or
@@ -639,7 +661,7 @@ __device__ __forceinline__ void stage_edge_segment(const Segment &S, const uint8
                                                    const uint8_t *hi)
 {
 #pragma unroll 1
-    for (int k = threadIdx.x; k < S.n16; k += kSegLanes) {
+    for (int k = seg_lane(); k < S.n16; k += kSegLanes) {
         const uint8_t *q = S.base + 16 * k;
         if (q >= lo && q + 16 <= hi) {
             *(uint4 *)(S.slot + 16 * k) = *(const uint4 *)q;
@@ -651,48 +673,66 @@ __device__ __forceinline__ void stage_edge_segment(const Segment &S, const uint8
     }
 }
 
-// Stage up to two segments with every global load of the lane issued before
-// any LDS write, so the wave waits for memory once per output row, not once
-// per chunk.  A lane handles chunks lane, lane + 64, ... (KMAX of them);
-// a lane past the segment re-reads its last chunk and writes into the slot's
-// slack (a slot holds 64 KMAX chunks), so the clean case has no divergent
-// branches at all.
-template <int KMAX>
-__device__ __forceinline__ void stage_pair(const Segment &A, const Segment &B,
-                                           const uint8_t *lo, const uint8_t *hi)
+// Staging is software-pipelined one output row deep: the 16-byte chunks of
+// the next row's segments are loaded into registers (issue_segment) before
+// the current row is blended and stored, and written to LDS (commit_segment)
+// at the top of the next iteration.  The wave therefore has the next row's
+// loads in flight while it computes and stores, instead of waiting for
+// memory once per row.  A lane handles chunks lane, lane + 64, ... (KMAX of
+// them); a lane past the segment re-reads its last chunk and writes into
+// the slot's slack (a slot holds 64 KMAX chunks), so the clean case has no
+// divergent branches at all.
+typedef unsigned int seg_v4u __attribute__((ext_vector_type(4)));
+
+template <int KMAX, bool NT>
+__device__ __forceinline__ void issue_segment(const Segment &S, seg_v4u (&v)[KMAX])
 {
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    const int lane = threadIdx.x;
-    const bool a_fast = A.on && A.clean, b_fast = B.on && B.clean;
-    v4u va[KMAX], vb[KMAX];
-    if (a_fast) {
+    if (S.on && S.clean) {
 #pragma unroll
         for (int i = 0; i < KMAX; ++i) {
-            const int k = min(lane + kSegLanes * i, A.n16 - 1);
-            va[i] = *(const v4u *)(A.base + 16 * k);
+            // (uniform) a round of chunks wholly past the segment loads nothing
+            if (kSegLanes * i < S.n16) {
+                const int k = min(seg_lane() + kSegLanes * i, S.n16 - 1);
+                const seg_v4u *q = (const seg_v4u *)(S.base + 16 * k);
+                if constexpr (NT) v[i] = __builtin_nontemporal_load(q);
+                else v[i] = *q;
+            }
         }
     }
-    if (b_fast) {
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            const int k = min(lane + kSegLanes * i, B.n16 - 1);
-            vb[i] = *(const v4u *)(B.base + 16 * k);
-        }
-    }
-    if (a_fast) {
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) *(v4u *)(A.slot + 16 * (lane + kSegLanes * i)) = va[i];
-    }
-    if (b_fast) {
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) *(v4u *)(B.slot + 16 * (lane + kSegLanes * i)) = vb[i];
-    }
-    if (A.on && !A.clean) stage_edge_segment(A, lo, hi);
-    if (B.on && !B.clean) stage_edge_segment(B, lo, hi);
 }
 
+template <int KMAX>
+__device__ __forceinline__ void commit_segment(const Segment &S, const seg_v4u (&v)[KMAX],
+                                               const uint8_t *lo, const uint8_t *hi)
+{
+    if (S.on) {
+        if (S.clean) {
+#pragma unroll
+            for (int i = 0; i < KMAX; ++i)
+                if (kSegLanes * i < S.n16)
+                    *(seg_v4u *)(S.slot + 16 * (seg_lane() + kSegLanes * i)) = v[i];
+        } else {
+            stage_edge_segment(S, lo, hi);
+        }
+    }
+}
+
+// What one output row needs from the staging step: the segments to stage,
+// where tap a of its two source rows sits in LDS, its row weight, and which
+// output row it is.
+struct RowPlan {
+    Segment A, B;
+    int la, lb;            // LDS byte offsets of column sa in the two source rows
+    unsigned wy1;          // uint8 row weight (11-bit)
+    float wyf;             // float row weight
+    long long n;           // output image
+    int dy;                // output row within the image
+};
+
 // Store N elements of one lane: vectorised when the chunk is whole and
-// aligned, element by element otherwise (row ends, odd pitches).
+// aligned, element by element otherwise (row ends, odd pitches).  The
+// stores are non-temporal: a resize writes its result once and never reads
+// it back, so it should not displace cached source rows.
 template <typename T, int N>
 __device__ __forceinline__ void store_chunk(T *out, const T (&v)[N], int valid)
 {
@@ -700,21 +740,21 @@ __device__ __forceinline__ void store_chunk(T *out, const T (&v)[N], int valid)
     if (valid == N && BYTES % 16 == 0 && ((uintptr_t)out & 15) == 0) {
 #pragma unroll
         for (int k = 0; k < BYTES / 16; ++k) {
-            uint4 q;
+            u32x4_t q;
             __builtin_memcpy(&q, (const uint8_t *)v + 16 * k, 16);
-            ((uint4 *)out)[k] = q;
+            __builtin_nontemporal_store(q, (u32x4_t *)out + k);
         }
     } else if (valid == N && BYTES % 4 == 0 && ((uintptr_t)out & 3) == 0) {
 #pragma unroll
         for (int k = 0; k < BYTES / 4; ++k) {
             uint32_t q;
             __builtin_memcpy(&q, (const uint8_t *)v + 4 * k, 4);
-            ((uint32_t *)out)[k] = q;
+            __builtin_nontemporal_store(q, (uint32_t *)out + k);
         }
     } else {
 #pragma unroll
         for (int k = 0; k < N; ++k)
-            if (k < valid) out[k] = v[k];
+            if (k < valid) __builtin_nontemporal_store(v[k], out + k);
     }
 }
 
@@ -744,102 +784,121 @@ struct RowStepper {
     }
 };
 
-template <typename T, int C, bool NEAREST, int KMAX, int OUT = kOutSame, bool ROI = false>
-__global__ __launch_bounds__(kSegLanes) void rowseg(
+template <typename T, int C, bool NEAREST, int KMAX, bool NT, int OUT = kOutSame, bool ROI = false>
+__global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff,
     const int32_t *__restrict__ rois)
 {
     T *const dst = (T *)dst_v;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
     constexpr int PX = SegShape<T, C>::PX;
     constexpr int PB = C * (int)sizeof(T);        // bytes per pixel
-    const int lane = threadIdx.x;
+    const int lane = seg_lane();
+    // wave index, made visibly uniform so that all per-row planning stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kSegLanes);
+    uint8_t *const lds = lds_all + (size_t)wave * 2 * seg_cap;   // this wave's two slots
     const int wx0 = blockIdx.x * kSegLanes * PX;  // first output column of the segment
     const int wx1 = min(wx0 + kSegLanes * PX, dW) - 1;
     const int x0 = wx0 + lane * PX;               // this lane's first output column
     const int valid_px = max(0, min(PX, dW - x0));
 
-    long long g = (long long)blockIdx.y * rows_per_block;
+    long long g = ((long long)blockIdx.y * kSegWaves + wave) * rows_per_block;
+    if (g >= rows_total) return;                  // a band past the last row
     long long g_end = g + rows_per_block;
     if (g_end > rows_total) g_end = rows_total;
-    long long n = g / dH;
-    int dy = (int)(g - n * dH);
+    const long long n0 = g / dH;
 
-    // The source region resized: the whole image, or image n's crop.
-    Crop crop{0, 0, W, H};
-    if constexpr (ROI) crop = load_crop(rois, n, H, W);
+    // Source columns [sa, sb] of a crop (relative to its left edge) touched
+    // by the segment's output columns.
+    auto seg_range = [&](const Crop &c, int &sa, int &sb) {
+        if constexpr (NEAREST) {
+            sa = nearest_index(wx0, c.w, dW);
+            sb = nearest_index(wx1, c.w, dW);
+        } else {
+            sa = axis_tap(wx0, c.w, dW).a;
+            sb = axis_tap(wx1, c.w, dW).b;
+        }
+    };
 
-    // Source columns touched by the segment, and this lane's column table:
-    // byte offset of tap a from column sa, whether tap b is the next column
-    // (it is not only where both taps clamp to the last column), and the
-    // weight of tap b.  Recomputed when a crop changes with the image.
-    int sa, sb;
+    // This lane's column table: byte offset of tap a from column sa, whether
+    // tap b is the next column (it is not only where both taps clamp to the
+    // last column), and the weight of tap b.  Recomputed when a crop changes
+    // with the image.
     int toff[PX];
     bool tnext[PX];
     unsigned tw[PX];
     float twf[PX];
-    auto column_table = [&]() {
-        const int cw = crop.w;
-        if constexpr (NEAREST) {
-            sa = nearest_index(wx0, cw, dW);
-            sb = nearest_index(wx1, cw, dW);
-        } else {
-            sa = axis_tap(wx0, cw, dW).a;
-            sb = axis_tap(wx1, cw, dW).b;
-        }
+    auto lane_table = [&](const Crop &c) {
+        int sa, sb;
+        seg_range(c, sa, sb);
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
             const int x = min(x0 + p, dW - 1);
             if constexpr (NEAREST) {
-                toff[p] = (nearest_index(x, cw, dW) - sa) * PB;
+                toff[p] = (nearest_index(x, c.w, dW) - sa) * PB;
                 tnext[p] = false;
                 tw[p] = 0;
                 twf[p] = 0.f;
             } else {
-                const Tap t = axis_tap(x, cw, dW);
+                const Tap t = axis_tap(x, c.w, dW);
                 toff[p] = (t.a - sa) * PB;
                 tnext[p] = t.b != t.a;
                 if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
                 else twf[p] = weightf(t);
             }
         }
-        sa += crop.x;
-        sb += crop.x;
     };
-    column_table();
-    int seg_bytes = (sb - sa + 1) * PB;
+
+    // The source region resized: the whole image, or image n's crop.
+    Crop crop{0, 0, W, H};
+    if constexpr (ROI) crop = load_crop(rois, n0, H, W);
+    lane_table(crop);
+
     const uint8_t *lo = (const uint8_t *)src;
     const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
     const size_t row_bytes = (size_t)W * PB;
     T *const out_lane = dst + (size_t)x0 * C;
 
+    // Planning state: the next output row to plan, its crop and segment.
+    long long pn = n0;
+    int pdy = (int)(g - n0 * dH);
+    int psa, pbytes;                 // first source column (absolute), bytes
+    auto set_segment = [&]() {
+        int sa, sb;
+        seg_range(crop, sa, sb);
+        psa = sa + crop.x;
+        pbytes = (sb - sa + 1) * PB;
+    };
+    set_segment();
     RowStepper ys;
-    ys.init(dy, crop.h, dH);
+    ys.init(pdy, crop.h, dH);
     // global source row held in each LDS slot, and its offset there
     long long held0 = -1, held1 = -1;
     int mis0 = 0, mis1 = 0;
 
-    for (; g < g_end; ++g) {
+    // Choose the source rows, weights and LDS slots of the planned row; the
+    // slots are claimed now, their contents land at the next commit.
+    auto plan_row = [&](RowPlan &P) {
         int ya, yb;
-        unsigned wy1 = 0;
-        float wyf = 0.f;
+        P.wy1 = 0;
+        P.wyf = 0.f;
         const int Hc = crop.h;
         if constexpr (NEAREST) {
             // nearest row: floor((2dy + 1) H / (2 dH)) = floor((num + dH) / den)
-            long long k = ys.q + ((ys.r + dH) >= ys.den ? 1 : 0);
-            ya = yb = (int)(k > Hc - 1 ? Hc - 1 : (k < 0 ? 0 : k));
+            const int k = ys.q + ((ys.r + dH) >= ys.den ? 1 : 0);
+            ya = yb = k > Hc - 1 ? Hc - 1 : (k < 0 ? 0 : k);
         } else {
-            const long long q = ys.q;
-            ya = (int)(q < 0 ? 0 : (q > Hc - 1 ? Hc - 1 : q));
-            yb = (int)(q + 1 < 0 ? 0 : (q + 1 > Hc - 1 ? Hc - 1 : q + 1));
+            const int q = ys.q;
+            ya = q < 0 ? 0 : (q > Hc - 1 ? Hc - 1 : q);
+            yb = q + 1 < 0 ? 0 : (q + 1 > Hc - 1 ? Hc - 1 : q + 1);
             Tap t;
-            t.r = (int)ys.r;
-            t.den = (int)ys.den;
-            if constexpr (sizeof(T) == 1) wy1 = weight11(t);
-            else wyf = weightf(t);
+            t.r = ys.r;
+            t.den = ys.den;
+            if constexpr (sizeof(T) == 1) P.wy1 = weight11(t);
+            else P.wyf = weightf(t);
         }
-        const long long ra = n * H + crop.y + ya, rb = n * H + crop.y + yb;
+        const long long ra = pn * H + crop.y + ya, rb = pn * H + crop.y + yb;
         int sa_slot = held0 == ra ? 0 : (held1 == ra ? 1 : -1);
         int sb_slot = held0 == rb ? 0 : (held1 == rb ? 1 : -1);
         const bool need_a = sa_slot < 0;
@@ -847,22 +906,61 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
         if (rb == ra) sb_slot = sa_slot;
         const bool need_b = sb_slot < 0;
         if (need_b) sb_slot = 1 - sa_slot;
-        Segment A, B;
-        A.plan(need_a, lds + sa_slot * seg_cap, lo + (size_t)ra * row_bytes + (size_t)sa * PB,
-               seg_bytes, lo, hi);
-        B.plan(need_b, lds + sb_slot * seg_cap, lo + (size_t)rb * row_bytes + (size_t)sa * PB,
-               seg_bytes, lo, hi);
-        stage_pair<KMAX>(A, B, lo, hi);
+        P.A.plan(need_a, lds + sa_slot * seg_cap, lo + (size_t)ra * row_bytes + (size_t)psa * PB,
+                 pbytes, lo, hi);
+        P.B.plan(need_b, lds + sb_slot * seg_cap, lo + (size_t)rb * row_bytes + (size_t)psa * PB,
+                 pbytes, lo, hi);
         if (need_a) {
-            if (sa_slot == 0) { held0 = ra; mis0 = A.mis; } else { held1 = ra; mis1 = A.mis; }
+            if (sa_slot == 0) { held0 = ra; mis0 = P.A.mis; } else { held1 = ra; mis1 = P.A.mis; }
         }
         if (need_b) {
-            if (sb_slot == 0) { held0 = rb; mis0 = B.mis; } else { held1 = rb; mis1 = B.mis; }
+            if (sb_slot == 0) { held0 = rb; mis0 = P.B.mis; } else { held1 = rb; mis1 = P.B.mis; }
         }
-        __syncthreads();
+        P.la = sa_slot * seg_cap + (sa_slot == 0 ? mis0 : mis1);
+        P.lb = sb_slot * seg_cap + (sb_slot == 0 ? mis0 : mis1);
+        P.n = pn;
+        P.dy = pdy;
+    };
+    // Step the planning state to the next output row.
+    auto advance = [&]() {
+        if (++pdy == dH) {
+            pdy = 0;
+            ++pn;
+            if constexpr (ROI) {
+                crop = load_crop(rois, pn, H, W);
+                set_segment();
+            }
+            ys.init(0, crop.h, dH);
+        } else {
+            ys.next();
+        }
+    };
 
-        const uint8_t *la = lds + sa_slot * seg_cap + (sa_slot == 0 ? mis0 : mis1);
-        const uint8_t *lb = lds + sb_slot * seg_cap + (sb_slot == 0 ? mis0 : mis1);
+    seg_v4u va[KMAX], vb[KMAX];
+    RowPlan P;
+    plan_row(P);
+    issue_segment<KMAX, NT>(P.A, va);
+    issue_segment<KMAX, NT>(P.B, vb);
+
+    for (; g < g_end; ++g) {
+        commit_segment<KMAX>(P.A, va, lo, hi);
+        commit_segment<KMAX>(P.B, vb, lo, hi);
+        wave_sync();
+
+        const uint8_t *la = lds + P.la;
+        const uint8_t *lb = lds + P.lb;
+        const unsigned wy1 = P.wy1;
+        const float wyf = P.wyf;
+        const long long n = P.n;
+        const int dy = P.dy;
+        const bool more = g + 1 < g_end;
+        if (more) {
+            advance();
+            plan_row(P);
+            issue_segment<KMAX, NT>(P.A, va);
+            issue_segment<KMAX, NT>(P.B, vb);
+        }
+
         T res[PX * C];
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
@@ -942,21 +1040,12 @@ __global__ __launch_bounds__(kSegLanes) void rowseg(
                 }
             }
         }
-        __syncthreads();
-        if (++dy == dH) {
-            dy = 0;
-            ++n;
-            if constexpr (ROI) {
-                if (g + 1 < g_end) {
-                    crop = load_crop(rois, n, H, W);
-                    column_table();
-                    seg_bytes = (sb - sa + 1) * PB;
-                }
-            }
-            ys.init(0, crop.h, dH);
-        } else {
-            ys.next();
+        // the next image's crop changes this lane's column table
+        if constexpr (ROI) {
+            if (more && P.n != n) lane_table(crop);
         }
+        // the compute above reads the LDS slots the next commit may overwrite
+        wave_sync();
     }
 }
 
