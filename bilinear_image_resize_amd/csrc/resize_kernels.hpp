@@ -758,8 +758,9 @@ __device__ __forceinline__ void store_chunk(T *out, const T (&v)[N], int valid)
     }
 }
 
-// Row map that steps from output row to output row without dividing.
-struct RowStepper {
+// Half-pixel map of one axis that steps from one output index to the next
+// without dividing (rows down a band, columns across a lane's pixels).
+struct AxisStepper {
     // all below 2^18: q in [-1, n_in], r < den = 2 n_out <= 131070
     int q, r;              // floor and remainder of num / den for the current row
     int dq, dr;            // 2 n_in = dq * den + dr
@@ -824,26 +825,35 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     // This lane's column table: byte offset of tap a from column sa, whether
     // tap b is the next column (it is not only where both taps clamp to the
     // last column), and the weight of tap b.  Recomputed when a crop changes
-    // with the image.
+    // with the image.  The lane's first column is mapped with one division;
+    // the next ones step from it exactly (the numerator grows by 2 n_in per
+    // column), and columns past the last output column repeat it.
     int toff[PX];
     bool tnext[PX];
     unsigned tw[PX];
     float twf[PX];
-    auto lane_table = [&](const Crop &c) {
-        int sa, sb;
-        seg_range(c, sa, sb);
+    auto lane_table = [&](const Crop &c, int sa) {
+        AxisStepper xs;
+        xs.init(min(x0, dW - 1), c.w, dW);
+        const int last = c.w - 1;
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
-            const int x = min(x0 + p, dW - 1);
+            if (p > 0 && x0 + p <= dW - 1) xs.next();
             if constexpr (NEAREST) {
-                toff[p] = (nearest_index(x, c.w, dW) - sa) * PB;
+                // floor((2x + 1) n_in / (2 n_out)) = floor((num + n_out) / den)
+                const int k = xs.q + ((xs.r + dW) >= xs.den ? 1 : 0);
+                toff[p] = (min(k, last) - sa) * PB;
                 tnext[p] = false;
                 tw[p] = 0;
                 twf[p] = 0.f;
             } else {
-                const Tap t = axis_tap(x, c.w, dW);
-                toff[p] = (t.a - sa) * PB;
-                tnext[p] = t.b != t.a;
+                const int a = min(max(xs.q, 0), last);
+                const int b = min(max(xs.q + 1, 0), last);
+                toff[p] = (a - sa) * PB;
+                tnext[p] = b != a;
+                Tap t;
+                t.r = xs.r;
+                t.den = xs.den;
                 if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
                 else twf[p] = weightf(t);
             }
@@ -853,7 +863,6 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     // The source region resized: the whole image, or image n's crop.
     Crop crop{0, 0, W, H};
     if constexpr (ROI) crop = load_crop(rois, n0, H, W);
-    lane_table(crop);
 
     const uint8_t *lo = (const uint8_t *)src;
     const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
@@ -863,15 +872,17 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     // Planning state: the next output row to plan, its crop and segment.
     long long pn = n0;
     int pdy = (int)(g - n0 * dH);
+    int seg_sa;                      // first source column, relative to the crop
     int psa, pbytes;                 // first source column (absolute), bytes
     auto set_segment = [&]() {
-        int sa, sb;
-        seg_range(crop, sa, sb);
-        psa = sa + crop.x;
-        pbytes = (sb - sa + 1) * PB;
+        int sb;
+        seg_range(crop, seg_sa, sb);
+        psa = seg_sa + crop.x;
+        pbytes = (sb - seg_sa + 1) * PB;
     };
     set_segment();
-    RowStepper ys;
+    lane_table(crop, seg_sa);
+    AxisStepper ys;
     ys.init(pdy, crop.h, dH);
     // global source row held in each LDS slot, and its offset there
     long long held0 = -1, held1 = -1;
@@ -1042,7 +1053,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         }
         // the next image's crop changes this lane's column table
         if constexpr (ROI) {
-            if (more && P.n != n) lane_table(crop);
+            if (more && P.n != n) lane_table(crop, seg_sa);
         }
         // the compute above reads the LDS slots the next commit may overwrite
         wave_sync();
