@@ -177,7 +177,8 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, SegPlan
     return true;
 }
 
-template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false>
+template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false,
+          int B = kBorderClamp>
 bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                 hipStream_t st, int &rc, const Affine &aff = Affine{},
                 const int32_t *rois = nullptr)
@@ -192,8 +193,12 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const int need = (pl.seg_cap / 16 + kSegLanes - 1) / kSegLanes;
     const int per_lane = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
     pl.seg_cap = per_lane * kSegLanes * 16;
+    // wrap adds 16 bytes in front of each slot and 16 behind it for the
+    // one-pixel halo around a staged row
+    const int slot_bytes = pl.seg_cap + (B == kBorderWrap ? 32 : 0);
+    if (2 * slot_bytes > kSegLdsBudget) return false;
     auto go = [&](auto kernel) {
-        return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), kSegWaves * 2 * pl.seg_cap, st,
+        return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), kSegWaves * 2 * slot_bytes, st,
                       (const T *)src, dst,
                       H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
                       (long long)batch * H * W * C, aff, rois);
@@ -206,12 +211,12 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const bool stream = NEAREST ? H >= dH : H >= 2 * dH;
     auto pick = [&](auto nt) {
         constexpr bool NT = decltype(nt)::value;
-        if (per_lane <= 1) return go(rowseg<T, C, NEAREST, 1, NT, OUT, ROI>);
-        if (per_lane <= 2) return go(rowseg<T, C, NEAREST, 2, NT, OUT, ROI>);
-        if (per_lane <= 4) return go(rowseg<T, C, NEAREST, 4, NT, OUT, ROI>);
-        return go(rowseg<T, C, NEAREST, 8, NT, OUT, ROI>);
+        if (per_lane <= 1) return go(rowseg<T, C, NEAREST, 1, NT, OUT, ROI, B>);
+        if (per_lane <= 2) return go(rowseg<T, C, NEAREST, 2, NT, OUT, ROI, B>);
+        if (per_lane <= 4) return go(rowseg<T, C, NEAREST, 4, NT, OUT, ROI, B>);
+        return go(rowseg<T, C, NEAREST, 8, NT, OUT, ROI, B>);
     };
-    if constexpr (!ROI) {
+    if constexpr (!ROI && B == kBorderClamp) {
         if (stream) {
             rc = pick(std::true_type{});
             return true;
@@ -330,6 +335,19 @@ int border_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
                     int border, hipStream_t st)
 {
     const long long rows = (long long)batch * dH;
+    const Path path = path_override();
+    const bool small = rows * dW < kSmallOutPixels;
+    if (path == Path::RowSeg || (path == Path::Auto && !small)) {
+        int rc;
+        if (border == MI_RESIZE_BORDER_MIRROR) {
+            if (try_rowseg<T, C, false, kOutSame, false, kBorderMirror>(src, dst, batch, H, W, dH,
+                                                                        dW, st, rc))
+                return rc;
+        } else if (try_rowseg<T, C, false, kOutSame, false, kBorderWrap>(src, dst, batch, H, W, dH,
+                                                                         dW, st, rc)) {
+            return rc;
+        }
+    }
     const Grid g = band_grid(rows, dW);
     const bool pix4 = C == 4 && aligned(src, 4 * sizeof(T)) && aligned(dst, 4 * sizeof(T));
     auto go = [&](auto kernel) {

@@ -717,6 +717,28 @@ __device__ __forceinline__ void commit_segment(const Segment &S, const seg_v4u (
     }
 }
 
+// LDS reads of a few bytes at any byte address.  Multi-byte LDS reads that
+// are not naturally aligned run far slower than aligned ones (a 2x uint8
+// upscale whose tap reads were unaligned dword reads took 36 us, the same
+// kernel with byte reads 16.7 us), so these read the aligned dwords around
+// the bytes and shift them into place.  They may read up to 3 bytes past
+// the last byte asked for (inside a slot's read slack).
+__device__ __forceinline__ uint32_t lds_bytes4(const uint8_t *p)
+{
+    const unsigned sh = (unsigned)(uintptr_t)p & 3u;
+    const uint32_t *w = (const uint32_t *)__builtin_assume_aligned(p - sh, 4);
+    return __builtin_amdgcn_alignbyte(w[1], w[0], sh);
+}
+
+__device__ __forceinline__ void lds_bytes8(const uint8_t *p, uint32_t &lo, uint32_t &hi)
+{
+    const unsigned sh = (unsigned)(uintptr_t)p & 3u;
+    const uint32_t *w = (const uint32_t *)__builtin_assume_aligned(p - sh, 4);
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    lo = __builtin_amdgcn_alignbyte(w1, w0, sh);
+    hi = __builtin_amdgcn_alignbyte(w2, w1, sh);
+}
+
 // What one output row needs from the staging step: the segments to stage,
 // where tap a of its two source rows sits in LDS, its row weight, and which
 // output row it is.
@@ -727,6 +749,7 @@ struct RowPlan {
     float wyf;             // float row weight
     long long n;           // output image
     int dy;                // output row within the image
+    const uint8_t *row_a, *row_b;   // wrap: start of the two source rows (halo)
 };
 
 // Store N elements of one lane: vectorised when the chunk is whole and
@@ -785,7 +808,46 @@ struct AxisStepper {
     }
 };
 
-template <typename T, int C, bool NEAREST, int KMAX, bool NT, int OUT = kOutSame, bool ROI = false>
+// Taps of one axis under border rule B, from the floor q and remainder r of
+// the exact coordinate num / den (an AxisStepper's state), n source pixels.
+// Clamp: the edge pixel repeats.  Mirror: the coordinate is first reflected
+// about the outermost pixel centres - in integers, so the remainder (and
+// with it the weight) is that of the reflected coordinate.  Wrap: the taps
+// stay unwrapped, a = q in [-1, n - 1] and b = a + 1 in [0, n]; the caller
+// reads column -1 as n - 1 and column n as 0 (shifting a coordinate by a
+// whole period leaves its remainder unchanged).
+template <int B>
+__device__ __forceinline__ void border_taps(int q, int r, int den, int n, int &a, int &b, int &rr)
+{
+    if constexpr (B == kBorderClamp) {
+        a = min(max(q, 0), n - 1);
+        b = min(max(q + 1, 0), n - 1);
+        rr = r;
+    } else if constexpr (B == kBorderMirror) {
+        if (n == 1) {
+            a = b = 0;
+            rr = 0;
+            return;
+        }
+        if (q < 0) {                                    // num < 0: num -> -num
+            q = r == 0 ? -q : -q - 1;
+            r = r == 0 ? 0 : den - r;
+        } else if (q > n - 1 || (q == n - 1 && r > 0)) {  // num > (n - 1) den
+            q = 2 * (n - 1) - q - (r > 0 ? 1 : 0);
+            r = r > 0 ? den - r : 0;
+        }
+        a = q;
+        b = min(q + 1, n - 1);
+        rr = r;
+    } else {
+        a = q;
+        b = q + 1;
+        rr = r;
+    }
+}
+
+template <typename T, int C, bool NEAREST, int KMAX, bool NT, int OUT = kOutSame, bool ROI = false,
+          int B = kBorderClamp>
 __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff,
@@ -795,10 +857,17 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
     constexpr int PX = SegShape<T, C>::PX;
     constexpr int PB = C * (int)sizeof(T);        // bytes per pixel
+    static_assert(B == kBorderClamp || (!NEAREST && !ROI && OUT == kOutSame),
+                  "mirror / wrap borders are for the plain linear resize");
+    // Wrap stages each row with a one-pixel halo: column -1 (= W - 1) in
+    // front of it, column W (= 0) behind it.  PAD bytes in front of the
+    // staged chunks hold the first; the slot's slack the second.
+    constexpr int PAD = B == kBorderWrap ? 16 : 0;
+    const int slot_bytes = seg_cap + 2 * PAD;
     const int lane = seg_lane();
     // wave index, made visibly uniform so that all per-row planning stays scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kSegLanes);
-    uint8_t *const lds = lds_all + (size_t)wave * 2 * seg_cap;   // this wave's two slots
+    uint8_t *const lds = lds_all + (size_t)wave * 2 * slot_bytes;   // this wave's two slots
     const int wx0 = blockIdx.x * kSegLanes * PX;  // first output column of the segment
     const int wx1 = min(wx0 + kSegLanes * PX, dW) - 1;
     const int x0 = wx0 + lane * PX;               // this lane's first output column
@@ -813,7 +882,19 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     // Source columns [sa, sb] of a crop (relative to its left edge) touched
     // by the segment's output columns.
     auto seg_range = [&](const Crop &c, int &sa, int &sb) {
-        if constexpr (NEAREST) {
+        if constexpr (B != kBorderClamp) {
+            // the taps of the first and last columns bound the segment's
+            // (mirror reflects at most the outermost columns onto the edge
+            // pixels; wrap's range is unwrapped, from -1 to W)
+            AxisStepper s0, s1;
+            s0.init(wx0, c.w, dW);
+            s1.init(wx1, c.w, dW);
+            int a0, b0, a1, b1, r;
+            border_taps<B>(s0.q, s0.r, s0.den, c.w, a0, b0, r);
+            border_taps<B>(s1.q, s1.r, s1.den, c.w, a1, b1, r);
+            sa = min(a0, a1);
+            sb = max(b0, b1);
+        } else if constexpr (NEAREST) {
             sa = nearest_index(wx0, c.w, dW);
             sb = nearest_index(wx1, c.w, dW);
         } else {
@@ -847,12 +928,13 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                 tw[p] = 0;
                 twf[p] = 0.f;
             } else {
-                const int a = min(max(xs.q, 0), last);
-                const int b = min(max(xs.q + 1, 0), last);
+                int a, b, rr;
+                border_taps<B>(xs.q, xs.r, xs.den, c.w, a, b, rr);
+                (void)last;
                 toff[p] = (a - sa) * PB;
                 tnext[p] = b != a;
                 Tap t;
-                t.r = xs.r;
+                t.r = rr;
                 t.den = xs.den;
                 if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
                 else twf[p] = weightf(t);
@@ -873,12 +955,21 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     long long pn = n0;
     int pdy = (int)(g - n0 * dH);
     int seg_sa;                      // first source column, relative to the crop
-    int psa, pbytes;                 // first source column (absolute), bytes
+    int psa, pbytes;                 // first staged source column (absolute), bytes
+    bool halo_l = false, halo_r = false;   // wrap: columns -1 and W are in the segment
     auto set_segment = [&]() {
         int sb;
         seg_range(crop, seg_sa, sb);
-        psa = seg_sa + crop.x;
-        pbytes = (sb - seg_sa + 1) * PB;
+        if constexpr (B == kBorderWrap) {
+            halo_l = seg_sa < 0;
+            halo_r = sb > crop.w - 1;
+            const int c0 = max(seg_sa, 0), c1 = min(sb, crop.w - 1);
+            psa = c0 + crop.x;
+            pbytes = (c1 - c0 + 1) * PB;
+        } else {
+            psa = seg_sa + crop.x;
+            pbytes = (sb - seg_sa + 1) * PB;
+        }
     };
     set_segment();
     lane_table(crop, seg_sa);
@@ -895,7 +986,17 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         P.wy1 = 0;
         P.wyf = 0.f;
         const int Hc = crop.h;
-        if constexpr (NEAREST) {
+        if constexpr (B != kBorderClamp) {
+            int qa, qb, rr;
+            border_taps<B>(ys.q, ys.r, ys.den, Hc, qa, qb, rr);
+            ya = qa < 0 ? qa + Hc : qa;               // wrap: row -1 is row H - 1
+            yb = qb > Hc - 1 ? qb - Hc : qb;          // wrap: row H is row 0
+            Tap t;
+            t.r = rr;
+            t.den = ys.den;
+            if constexpr (sizeof(T) == 1) P.wy1 = weight11(t);
+            else P.wyf = weightf(t);
+        } else if constexpr (NEAREST) {
             // nearest row: floor((2dy + 1) H / (2 dH)) = floor((num + dH) / den)
             const int k = ys.q + ((ys.r + dH) >= ys.den ? 1 : 0);
             ya = yb = k > Hc - 1 ? Hc - 1 : (k < 0 ? 0 : k);
@@ -917,18 +1018,24 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         if (rb == ra) sb_slot = sa_slot;
         const bool need_b = sb_slot < 0;
         if (need_b) sb_slot = 1 - sa_slot;
-        P.A.plan(need_a, lds + sa_slot * seg_cap, lo + (size_t)ra * row_bytes + (size_t)psa * PB,
-                 pbytes, lo, hi);
-        P.B.plan(need_b, lds + sb_slot * seg_cap, lo + (size_t)rb * row_bytes + (size_t)psa * PB,
-                 pbytes, lo, hi);
+        P.A.plan(need_a, lds + sa_slot * slot_bytes + PAD,
+                 lo + (size_t)ra * row_bytes + (size_t)psa * PB, pbytes, lo, hi);
+        P.B.plan(need_b, lds + sb_slot * slot_bytes + PAD,
+                 lo + (size_t)rb * row_bytes + (size_t)psa * PB, pbytes, lo, hi);
+        if constexpr (B == kBorderWrap) {
+            P.row_a = lo + (size_t)ra * row_bytes;
+            P.row_b = lo + (size_t)rb * row_bytes;
+        }
         if (need_a) {
             if (sa_slot == 0) { held0 = ra; mis0 = P.A.mis; } else { held1 = ra; mis1 = P.A.mis; }
         }
         if (need_b) {
             if (sb_slot == 0) { held0 = rb; mis0 = P.B.mis; } else { held1 = rb; mis1 = P.B.mis; }
         }
-        P.la = sa_slot * seg_cap + (sa_slot == 0 ? mis0 : mis1);
-        P.lb = sb_slot * seg_cap + (sb_slot == 0 ? mis0 : mis1);
+        // LDS offset of column sa: the staged bytes start at column psa
+        const int front = B == kBorderWrap && halo_l ? PB : 0;
+        P.la = sa_slot * slot_bytes + PAD + (sa_slot == 0 ? mis0 : mis1) - front;
+        P.lb = sb_slot * slot_bytes + PAD + (sb_slot == 0 ? mis0 : mis1) - front;
         P.n = pn;
         P.dy = pdy;
     };
@@ -947,15 +1054,43 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         }
     };
 
+    // Wrap halo bytes: lanes 0 .. PB-1 carry column W - 1 of a staged row,
+    // lanes 32 .. 32+PB-1 its column 0; loaded with the row, written after it.
+    const bool halo_lane = (lane < PB && halo_l) || (lane >= 32 && lane < 32 + PB && halo_r);
+    auto halo_load = [&](const Segment &S, const uint8_t *row) -> unsigned {
+        if constexpr (B == kBorderWrap) {
+            if (S.on && halo_lane)
+                return lane < 32 ? row[(size_t)(W - 1) * PB + lane] : row[lane - 32];
+        }
+        return 0;
+    };
+    auto halo_store = [&](const Segment &S, unsigned v) {
+        if constexpr (B == kBorderWrap) {
+            if (S.on && halo_lane) {
+                if (lane < 32) S.slot[S.mis - PB + lane] = (uint8_t)v;
+                else S.slot[S.mis + pbytes + lane - 32] = (uint8_t)v;
+            }
+        }
+    };
+
     seg_v4u va[KMAX], vb[KMAX];
+    unsigned ha = 0, hb = 0;
     RowPlan P;
     plan_row(P);
     issue_segment<KMAX, NT>(P.A, va);
     issue_segment<KMAX, NT>(P.B, vb);
+    if constexpr (B == kBorderWrap) {
+        ha = halo_load(P.A, P.row_a);
+        hb = halo_load(P.B, P.row_b);
+    }
 
     for (; g < g_end; ++g) {
         commit_segment<KMAX>(P.A, va, lo, hi);
         commit_segment<KMAX>(P.B, vb, lo, hi);
+        if constexpr (B == kBorderWrap) {
+            halo_store(P.A, ha);
+            halo_store(P.B, hb);
+        }
         wave_sync();
 
         const uint8_t *la = lds + P.la;
@@ -970,6 +1105,10 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             plan_row(P);
             issue_segment<KMAX, NT>(P.A, va);
             issue_segment<KMAX, NT>(P.B, vb);
+            if constexpr (B == kBorderWrap) {
+                ha = halo_load(P.A, P.row_a);
+                hb = halo_load(P.B, P.row_b);
+            }
         }
 
         T res[PX * C];
@@ -988,19 +1127,17 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                     // tap a = bytes [0, C), tap b = bytes [C, 2C) of the word
                     // (or tap a again where both taps clamp to one column)
                     uint32_t a_lo, a_hi, b_lo, b_hi;
-                    if constexpr (2 * PB <= 4) {
-                        __builtin_memcpy(&a_lo, la + toff[p], 4);
-                        __builtin_memcpy(&b_lo, lb + toff[p], 4);
-                        a_hi = a_lo;
-                        b_hi = b_lo;
+                    if constexpr (C == 1) {
+                        // two byte reads beat one shifted dword pair here
+                        const uint8_t *pa = la + toff[p], *pb = lb + toff[p];
+                        a_lo = a_hi = (uint32_t)pa[0] | ((uint32_t)pa[1] << 8);
+                        b_lo = b_hi = (uint32_t)pb[0] | ((uint32_t)pb[1] << 8);
+                    } else if constexpr (2 * PB <= 4) {
+                        a_lo = a_hi = lds_bytes4(la + toff[p]);
+                        b_lo = b_hi = lds_bytes4(lb + toff[p]);
                     } else {
-                        uint64_t wa, wb;
-                        __builtin_memcpy(&wa, la + toff[p], 8);
-                        __builtin_memcpy(&wb, lb + toff[p], 8);
-                        a_lo = (uint32_t)wa;
-                        a_hi = (uint32_t)(wa >> 32);
-                        b_lo = (uint32_t)wb;
-                        b_hi = (uint32_t)(wb >> 32);
+                        lds_bytes8(la + toff[p], a_lo, a_hi);
+                        lds_bytes8(lb + toff[p], b_lo, b_hi);
                     }
                     // the second tap's C bytes, shifted down to byte 0
                     const uint32_t a2 = tnext[p] ? __builtin_amdgcn_alignbyte(a_hi, a_lo, C % 4 == 0 ? 0 : C)
@@ -1016,9 +1153,19 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                         res[p * C + c] = (T)blend_u8(p00, p01, p10, p11, tw[p], wy1);
                     }
                 } else {
+                    // float taps sit at 4-byte aligned LDS addresses (the
+                    // source is 4-byte aligned and so is every pixel), which
+                    // lets C = 1 and 3 read dword pairs.  RGBA pixels are
+                    // 16 bytes and, with a 16-byte aligned source (the usual
+                    // case), 16-byte aligned, so they keep 16-byte reads.
                     T ra2[2 * C], rb2[2 * C];
-                    __builtin_memcpy(ra2, la + toff[p], 2 * PB);
-                    __builtin_memcpy(rb2, lb + toff[p], 2 * PB);
+                    if constexpr (PB % 16 == 0) {
+                        __builtin_memcpy(ra2, la + toff[p], 2 * PB);
+                        __builtin_memcpy(rb2, lb + toff[p], 2 * PB);
+                    } else {
+                        __builtin_memcpy(ra2, __builtin_assume_aligned(la + toff[p], 4), 2 * PB);
+                        __builtin_memcpy(rb2, __builtin_assume_aligned(lb + toff[p], 4), 2 * PB);
+                    }
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         const T a0 = ra2[c], a1 = tnext[p] ? ra2[C + c] : ra2[c];

@@ -453,13 +453,16 @@ def test_roi_random(dtype, path, monkeypatch):
 # --------------------------------------------------------------------------
 # border rules (mirror, wrap)
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
 @pytest.mark.parametrize("border", ["mirror", "wrap"])
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
-def test_border_modes(border, dtype):
+def test_border_modes(border, dtype, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
     r = np.random.default_rng(717 + (dtype == "f32") + 2 * (border == "wrap"))
     shapes = [random_case(r) for _ in range(40)] + EDGE[:14] + [(1, 3, 3, 1, 6144, 6144 // 2048 * 3)]
     for i, (N, H, W, C, dH, dW) in enumerate(shapes):
-        say("case border %s %s #%d %s" % (border, dtype, i, (N, H, W, C, dH, dW)))
+        say("case border %s %s %s #%d %s" % (border, dtype, path, i, (N, H, W, C, dH, dW)))
         s = random_image(r, (N, H, W, C), dtype)
         src = torch.from_numpy(s).cuda()
         dst = torch.empty((N, dH, dW, C), dtype=src.dtype, device="cuda")
@@ -467,3 +470,18 @@ def test_border_modes(border, dtype):
         torch.cuda.synchronize()
         assert_parity(dst.cpu().numpy(), oracle.resize_linear(s, dH, dW, border=border),
                       "border %s #%d %s" % (border, i, (N, H, W, C, dH, dW)))
+
+
+@pytest.mark.parametrize("border", ["mirror", "wrap"])
+def test_border_thumb_full_size(border):
+    """The thumbnail batch (256 x 480x640x3 -> 224x224) under each border rule,
+    in the launch configuration the benchmark times; every image compared."""
+    w = WORKLOADS["thumb"]
+    say("case border full size %s %s -> %s" % (border, w.src_shape, w.dst_shape))
+    s = make_source(w)
+    src = torch.from_numpy(s).cuda()
+    dst = torch.empty(w.dst_shape, dtype=src.dtype, device="cuda")
+    R.resize_linear_border(src, dst, border=border)
+    torch.cuda.synchronize()
+    assert_parity(dst.cpu().numpy(), oracle.resize_linear(s, w.dH, w.dW, border=border),
+                  "border %s thumb" % border)
