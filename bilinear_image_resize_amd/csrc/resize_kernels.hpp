@@ -1115,8 +1115,16 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
             if constexpr (NEAREST) {
+                // one pixel, read with aligned accesses (see lds_bytes4)
                 T v[C];
-                __builtin_memcpy(v, la + toff[p], PB);
+                if constexpr (sizeof(T) == 1 && C > 1) {
+                    const uint32_t w = lds_bytes4(la + toff[p]);
+                    __builtin_memcpy(v, &w, PB);
+                } else if constexpr (sizeof(T) == 1 || PB % 16 == 0) {
+                    __builtin_memcpy(v, la + toff[p], PB);
+                } else {
+                    __builtin_memcpy(v, __builtin_assume_aligned(la + toff[p], 4), PB);
+                }
 #pragma unroll
                 for (int c = 0; c < C; ++c) res[p * C + c] = v[c];
             } else {
