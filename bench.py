@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--graph", type=int, default=0, metavar="B",
                    help="informational: also time the steps captured B at a time into a HIP "
                         "graph and replayed (small-image latency)")
+    p.add_argument("--no-copy", action="store_true",
+                   help="skip the copy-kernel ceiling at the same bytes per launch")
     p.add_argument("--no-pipelined", action="store_true",
                    help="skip the extra two-stream pipelined measurement")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -106,6 +108,54 @@ def copy_calibration(args):
     us = e0.elapsed_time(e1) * 1e3 / args.steps
     print(json.dumps({"copy_bytes": n, "pairs": pairs, "kernel_us": round(us, 3),
                       "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
+
+
+def device_hbm_peak(dev_index=0):
+    """Peak HBM bandwidth as the HIP runtime reports the memory interface:
+    hipDeviceGetAttribute's memory bus width (bits, attribute 59) and peak
+    memory clock (kHz, attribute 60), at two transfers per clock.  A cross-check
+    of the published 8 TB/s, not a replacement for it."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    bus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(bus), 59, dev_index) != 0:
+        return None
+    if hip.hipDeviceGetAttribute(ctypes.byref(clk), 60, dev_index) != 0:
+        return None
+    return {"bus_bits": bus.value, "mem_clock_khz": clk.value,
+            "GBps_at_2_per_clock": round(2 * clk.value * 1e3 * bus.value / 8 / 1e9, 1)}
+
+
+def copy_same_bytes(total_bytes, steps, lib, dev, sh):
+    """A plain 16-byte copy kernel moving the same bytes per launch as one
+    resize (total_bytes / 2 read + total_bytes / 2 written), over rotating
+    buffers that defeat the Infinity Cache, timed like the resize."""
+    import torch
+
+    n = (total_bytes // 2 + 15) // 16 * 16
+    pairs = max(2, -(-2 * INFINITY_CACHE_BYTES // (2 * n)))
+    bufs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(k & 255),
+             torch.empty(n, dtype=torch.uint8, device=dev)) for k in range(pairs)]
+    ptrs = [(a.data_ptr(), b.data_ptr()) for a, b in bufs]
+    for i in range(2 * pairs):
+        lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    bad = 0
+    for i in range(steps):
+        bad |= lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    if bad:
+        raise RuntimeError("resize_copy_bytes failed (%d)" % bad)
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del bufs
+    return {"bytes_moved": 2 * n, "kernel_us": round(us, 3), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(w, src_np, mode, budget_s):
@@ -381,6 +431,16 @@ def main():
             "traffic": traffic,
         },
     }
+    # the copy-kernel ceiling at the same bytes per launch, and the HBM peak
+    # the runtime reports (both informational)
+    if not args.no_copy:
+        cp = copy_same_bytes(pair_bytes, min(K, 500), R._load(), dev,
+                             torch.cuda.current_stream(dev).cuda_stream)
+        cp["resize_frac_of_copy"] = round(achieved / cp["GBps"], 4)
+        line["copy_same_bytes"] = cp
+    peak_dev = device_hbm_peak()
+    if peak_dev:
+        line["hbm_peak_device"] = peak_dev
     if pipelined:
         line["pipelined_two_streams"] = pipelined
     if graphed:

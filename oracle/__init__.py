@@ -63,6 +63,8 @@ def _load():
             f.restype = ci
         lib.oracle_nearest.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, i64, i64]
         lib.oracle_nearest.restype = ci
+        lib.oracle_nearest_map.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, i64, i64, ci]
+        lib.oracle_nearest_map.restype = ci
         _lib = lib
     return _lib
 
@@ -165,14 +167,23 @@ def resize_linear_roi(src: np.ndarray, rois, dH: int, dW: int) -> np.ndarray:
     return out
 
 
-def resize_nearest(src: np.ndarray, dH: int, dW: int, rows=None) -> np.ndarray:
-    """Nearest-neighbour resize of an NHWC array (any element type) to dH x dW."""
+NEAREST_MAPPINGS = {"half_pixel": 0, "floor": 1, "round": 2}
+
+
+def resize_nearest(src: np.ndarray, dH: int, dW: int, rows=None,
+                   mapping: str = "half_pixel") -> np.ndarray:
+    """Nearest-neighbour resize of an NHWC array (any element type) to dH x dW.
+
+    ``mapping``: "half_pixel" (default; pixel centres, rounded half up),
+    "floor" (corner-aligned x = d * n_in / n_out, floored: the legacy nearest)
+    or "round" (the same coordinate rounded half up, as hnwysp.cn news/129086
+    s3.2's kernel does), each clamped to the image."""
     src = _as_nhwc(src)
     N, H, W, C = src.shape
     r0, r1 = _rows(N, dH, rows)
     full = np.empty((N * dH, dW, C), dtype=src.dtype)
-    rc = _load().oracle_nearest(src.ctypes.data, full.ctypes.data, src.itemsize,
-                                N, H, W, C, dH, dW, r0, r1)
+    rc = _load().oracle_nearest_map(src.ctypes.data, full.ctypes.data, src.itemsize,
+                                    N, H, W, C, dH, dW, r0, r1, NEAREST_MAPPINGS[mapping])
     if rc != 0:
         raise ValueError("oracle rejected arguments (code %d)" % rc)
     if rows is not None:

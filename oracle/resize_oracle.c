@@ -41,7 +41,10 @@
  *  - float32: u, v and the four-term sum of [P3] s2.2 are evaluated in double
  *    and rounded to float once.
  *  - Nearest: the same half-pixel map, then round half up ([P3] s2.1 rounds to
- *    the nearest pixel), then clamp ([P3] s3.2 / s6.1).
+ *    the nearest pixel), then clamp ([P3] s3.2 / s6.1).  Two corner-aligned
+ *    mappings are offered beside it (oracle_nearest_map): [P3] s3.2's kernel
+ *    as printed, x = dx / scale rounded half up; and the same coordinate
+ *    taken with floor, the legacy nearest of image libraries.
  *
  * Layout: src is N x H x W x C (interleaved channels, "HWC" per image),
  * dst is N x dH x dW x C, both contiguous.  Output rows are numbered
@@ -242,9 +245,36 @@ static int64_t nearest_index(int64_t d, int64_t in_len, int64_t out_len)
     return k;
 }
 
-int oracle_nearest(const void *src_v, void *dst_v, int elem_bytes,
-                   int N, int H, int W, int C, int dH, int dW,
-                   int64_t row_begin, int64_t row_end)
+/*
+ * Corner-aligned nearest ([P3] s3.2: the source coordinate is dx / scale with
+ * scale = out_len / in_len, no half-pixel shift): x = d * in_len / out_len.
+ *   NEAREST_ROUND  round x half up, as [P3] s3.2's kernel does
+ *                  (floor(x + 0.5)), then clamp to the image;
+ *   NEAREST_FLOOR  floor(x), which never leaves the image.
+ */
+enum { NEAREST_HALF_PIXEL = 0, NEAREST_FLOOR = 1, NEAREST_ROUND = 2 };
+
+static int64_t nearest_index_corner(int64_t d, int64_t in_len, int64_t out_len, int mapping)
+{
+    int64_t k;
+    if (mapping == NEAREST_FLOOR)
+        k = floor_div(d * in_len, out_len);
+    else
+        k = floor_div(2 * d * in_len + out_len, 2 * out_len);   /* floor(x + 1/2) */
+    if (k > in_len - 1) k = in_len - 1;
+    return k;
+}
+
+static int64_t nearest_index_map(int64_t d, int64_t in_len, int64_t out_len, int mapping)
+{
+    if (mapping == NEAREST_HALF_PIXEL)
+        return nearest_index(d, in_len, out_len);
+    return nearest_index_corner(d, in_len, out_len, mapping);
+}
+
+int oracle_nearest_map(const void *src_v, void *dst_v, int elem_bytes,
+                       int N, int H, int W, int C, int dH, int dW,
+                       int64_t row_begin, int64_t row_end, int mapping)
 {
     const unsigned char *src = (const unsigned char *)src_v;
     unsigned char *dst = (unsigned char *)dst_v;
@@ -253,12 +283,14 @@ int oracle_nearest(const void *src_v, void *dst_v, int elem_bytes,
         return 1;
     if (row_begin < 0 || row_end > (int64_t)N * dH || row_begin > row_end)
         return 2;
+    if (mapping < NEAREST_HALF_PIXEL || mapping > NEAREST_ROUND)
+        return 3;
     size_t px = (size_t)C * (size_t)elem_bytes;
     for (int64_t r = row_begin; r < row_end; ++r) {
         int64_t n = r / dH, y = r % dH;
-        int64_t sy = nearest_index(y, H, dH);
+        int64_t sy = nearest_index_map(y, H, dH, mapping);
         for (int64_t x = 0; x < dW; ++x) {
-            int64_t sx = nearest_index(x, W, dW);
+            int64_t sx = nearest_index_map(x, W, dW, mapping);
             const unsigned char *from =
                 src + (((size_t)n * H + sy) * W + sx) * px;
             unsigned char *to = dst + (((size_t)n * dH + y) * dW + x) * px;
@@ -267,4 +299,12 @@ int oracle_nearest(const void *src_v, void *dst_v, int elem_bytes,
         }
     }
     return 0;
+}
+
+int oracle_nearest(const void *src_v, void *dst_v, int elem_bytes,
+                   int N, int H, int W, int C, int dH, int dW,
+                   int64_t row_begin, int64_t row_end)
+{
+    return oracle_nearest_map(src_v, dst_v, elem_bytes, N, H, W, C, dH, dW, row_begin, row_end,
+                              NEAREST_HALF_PIXEL);
 }

@@ -36,6 +36,12 @@ MUTANTS = {
                           "            num = 2 * (in_len - 1) * den - num - den;"),
     "wrap_neighbour_clamped": ("        return (i + 1 < len) ? (i + 1) : 0;",
                                "        return (i + 1 < len) ? (i + 1) : (len - 1);"),
+    # the corner-aligned floor mapping rounding instead of flooring
+    "corner_floor_rounds": ("k = floor_div(d * in_len, out_len);",
+                            "k = floor_div(2 * d * in_len + out_len, 2 * out_len);"),
+    # the corner-aligned round mapping rounding halves down
+    "corner_round_half_down": ("k = floor_div(2 * d * in_len + out_len, 2 * out_len);   /* floor(x + 1/2) */",
+                               "k = floor_div(2 * d * in_len + out_len - 1, 2 * out_len);"),
 }
 # (truncating instead of flooring the division is an equivalent mutant: the
 # coordinate is clamped to be non-negative before it is divided.)

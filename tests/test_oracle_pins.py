@@ -295,6 +295,82 @@ def test_nearest_matches_torch_nearest_exact():
 
 
 # --------------------------------------------------------------------------
+# nearest, corner-aligned mappings: "floor" (legacy) and "round" (the CUDA
+# kernel of hnwysp.cn news/129086 s3.2: x = d / scale, floor(x + 0.5))
+# --------------------------------------------------------------------------
+def test_nearest_mappings_by_hand():
+    """S = 16 (4y + x), resized 4x4 -> 3x3: the source coordinate of output d
+    is 4d/3 = 0, 1.33, 2.67 (corner-aligned) or (d + 1/2) 4/3 - 1/2 =
+    0.17, 1.5, 2.83 (half-pixel); floor gives columns 0, 1, 2, round half up
+    0, 1, 3, and the half-pixel map rounded half up 0, 2, 3.  4x4 -> 2x2:
+    corner-aligned 0, 2 for both floor and round, half-pixel 1, 3."""
+    S = (16 * (4 * np.arange(4)[:, None] + np.arange(4)[None, :])).astype(np.uint8)
+    idx = {"floor": [0, 1, 2], "round": [0, 1, 3], "half_pixel": [0, 2, 3]}
+    for m, cols in idx.items():
+        out = oracle.resize_nearest(S, 3, 3, mapping=m)[0, :, :, 0]
+        assert out.tolist() == [[16 * (4 * y + x) for x in cols] for y in cols], m
+    half = {"floor": [0, 2], "round": [0, 2], "half_pixel": [1, 3]}
+    for m, cols in half.items():
+        out = oracle.resize_nearest(S, 2, 2, mapping=m)[0, :, :, 0]
+        assert out.tolist() == [[16 * (4 * y + x) for x in cols] for y in cols], m
+
+
+def test_nearest_mappings_identity_and_upscale():
+    """At scale 1 every mapping is the identity.  For an integer upscale k,
+    floor picks d // k (replication, like the half-pixel map), and round
+    picks floor(d / k + 1/2), clamped to the last pixel."""
+    r = rng(13)
+    s = rand_img(r, (2, 9, 7, 3), np.uint8)
+    for m in ("floor", "round"):
+        assert np.array_equal(oracle.resize_nearest(s, 9, 7, mapping=m), s)
+    for k in (2, 3, 5):
+        out = oracle.resize_nearest(s, 9 * k, 7 * k, mapping="floor")
+        assert np.array_equal(out, s.repeat(k, axis=1).repeat(k, axis=2))
+        out = oracle.resize_nearest(s, 9 * k, 7 * k, mapping="round")
+        ys = np.minimum((2 * np.arange(9 * k) + k) // (2 * k), 8)
+        xs = np.minimum((2 * np.arange(7 * k) + k) // (2 * k), 6)
+        assert np.array_equal(out, s[:, ys][:, :, xs])
+
+
+def test_nearest_floor_matches_torch_nearest():
+    """torch's legacy "nearest" takes floor(d * in / out) in floating point;
+    where the exact value is an integer its rounding may land one pixel low,
+    so those rows and columns are left out (the cases above cover them)."""
+    r = rng(14)
+    compared = 0
+    for _ in range(200):
+        H, W = (int(v) for v in r.integers(1, 40, size=2))
+        dH, dW = (int(v) for v in r.integers(1, 60, size=2))
+        s = rand_img(r, (1, H, W, 2), np.float32)
+        t = torch.from_numpy(s.astype(np.float64)).permute(0, 3, 1, 2)
+        ref = torch.nn.functional.interpolate(t, size=(dH, dW), mode="nearest")
+        ref = ref.permute(0, 2, 3, 1).numpy().astype(np.float32)
+        out = oracle.resize_nearest(s, dH, dW, mapping="floor")
+        rows = [d for d in range(dH) if (Fraction(d) * Fraction(H, dH)).denominator != 1]
+        cols = [d for d in range(dW) if (Fraction(d) * Fraction(W, dW)).denominator != 1]
+        sub = np.ix_([0], rows, cols, [0, 1])
+        assert np.array_equal(out[sub], ref[sub])
+        compared += len(rows) * len(cols)
+    assert compared > 50000
+
+
+def test_nearest_round_brute_force():
+    """round: the exact coordinate d * in / out as a Fraction, rounded half up
+    and clamped, on small shapes."""
+    r = rng(15)
+    for _ in range(60):
+        H, W = (int(v) for v in r.integers(1, 12, size=2))
+        dH, dW = (int(v) for v in r.integers(1, 20, size=2))
+        s = rand_img(r, (1, H, W, 1), np.uint8)
+        out = oracle.resize_nearest(s, dH, dW, mapping="round")
+        for y in range(dH):
+            sy = min(int(Fraction(y * H, dH) + Fraction(1, 2)), H - 1)
+            for x in range(dW):
+                sx = min(int(Fraction(x * W, dW) + Fraction(1, 2)), W - 1)
+                assert out[0, y, x, 0] == s[0, sy, sx, 0]
+
+
+# --------------------------------------------------------------------------
 # layout invariants: transpose, horizontal flip, channels, batch
 # --------------------------------------------------------------------------
 def test_transpose_equivariance():
