@@ -111,10 +111,12 @@ def copy_calibration(args):
 
 
 def device_hbm_peak(dev_index=0):
-    """Peak HBM bandwidth as the HIP runtime reports the memory interface:
-    hipDeviceGetAttribute's memory bus width (bits, attribute 59) and peak
-    memory clock (kHz, attribute 60), at two transfers per clock.  A cross-check
-    of the published 8 TB/s, not a replacement for it."""
+    """Peak HBM bandwidth from the memory interface the HIP runtime reports:
+    hipDeviceGetAttribute's memory bus width (bits, attribute 59) and memory
+    clock (kHz, attribute 60).  HBM3E moves 4 bits per pin per reported clock
+    (its data clock runs at twice the reported one, double data rate), so
+    8192 bits x 2 GHz x 4 / 8 = 8192 GB/s.  A cross-check of the published
+    8 TB/s, not a replacement for it."""
     import ctypes
     try:
         hip = ctypes.CDLL("libamdhip64.so")
@@ -126,7 +128,7 @@ def device_hbm_peak(dev_index=0):
     if hip.hipDeviceGetAttribute(ctypes.byref(clk), 60, dev_index) != 0:
         return None
     return {"bus_bits": bus.value, "mem_clock_khz": clk.value,
-            "GBps_at_2_per_clock": round(2 * clk.value * 1e3 * bus.value / 8 / 1e9, 1)}
+            "GBps_at_4_per_clock": round(4 * clk.value * 1e3 * bus.value / 8 / 1e9, 1)}
 
 
 def copy_same_bytes(total_bytes, steps, lib, dev, sh):

@@ -35,7 +35,7 @@ _LIB_PATH = os.path.join(_PKG, "libmi_resize.so")
 
 U8 = 0
 F32 = 1
-_ABI_VERSION = 4
+_ABI_VERSION = 5
 
 _lib = None
 
@@ -80,6 +80,8 @@ def _load():
     lib.resize_linear_roi.restype = ci
     lib.resize_linear_border.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, vp]
     lib.resize_linear_border.restype = ci
+    lib.resize_nearest_mapping.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.resize_nearest_mapping.restype = ci
     if lib.resize_abi_version() != _ABI_VERSION:
         raise RuntimeError("libmi_resize.so ABI version %d, binding expects %d"
                            % (lib.resize_abi_version(), _ABI_VERSION))
@@ -238,6 +240,27 @@ def resize_linear_border(src, dst, border="mirror", stream=None):
                                       dH, dW, BORDERS[border], _stream_handle(stream, src.device))
     if rc != 0:
         raise ResizeError(rc, "resize_linear_border")
+    return dst
+
+
+NEAREST_MAPPINGS = {"half_pixel": 0, "floor": 1, "round": 2}
+
+
+def resize_nearest_mapping(src, dst, mapping="floor", stream=None):
+    """Nearest-neighbour resize with a coordinate mapping: "half_pixel" (as
+    resize_nearest), "floor" (floor(d * in / out), the legacy nearest) or
+    "round" (floor(d * in / out + 1/2)); see include/mi_resize.h."""
+    if mapping not in NEAREST_MAPPINGS:
+        raise ValueError("mapping must be one of %s" % sorted(NEAREST_MAPPINGS))
+    N, H, W, C = _nhwc(src, "src")
+    N2, dH, dW, C2 = _nhwc(dst, "dst")
+    if (N2, C2) != (N, C) or src.dim() != dst.dim() or src.dtype != dst.dtype:
+        raise ValueError("src %s / dst %s mismatch" % (tuple(src.shape), tuple(dst.shape)))
+    rc = _load().resize_nearest_mapping(src.data_ptr(), dst.data_ptr(), N, H, W, C, _dtype_code(src),
+                                        dH, dW, NEAREST_MAPPINGS[mapping],
+                                        _stream_handle(stream, src.device))
+    if rc != 0:
+        raise ResizeError(rc, "resize_nearest_mapping")
     return dst
 
 

@@ -181,7 +181,7 @@ template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false,
           int B = kBorderClamp>
 bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                 hipStream_t st, int &rc, const Affine &aff = Affine{},
-                const int32_t *rois = nullptr)
+                const int32_t *rois = nullptr, int nn_map = kNearestHalfPixel)
 {
     const long long rows = (long long)batch * dH;
     SegPlan pl;
@@ -201,7 +201,7 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
         return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), kSegWaves * 2 * slot_bytes, st,
                       (const T *)src, dst,
                       H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
-                      (long long)batch * H * W * C, aff, rois);
+                      (long long)batch * H * W * C, aff, rois, nn_map);
     };
     // Non-temporal staging loads when no source row is used by two output
     // rows (a row step of at least 2 for linear, 1 for nearest): nothing
@@ -251,13 +251,13 @@ bool up2_path_fits(int C, int H, int W, int dH, int dW, const void *src, const v
 
 template <int BPP>
 int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                   hipStream_t st)
+                   int map, hipStream_t st)
 {
     const long long rows = (long long)batch * dH;
     const Grid g = band_grid(rows, dW);
     auto go = [&](auto kernel) {
         return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const uint8_t *)src,
-                      (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks);
+                      (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks, map);
     };
     if constexpr (BPP % 16 == 0) {
         if (aligned(src, 16) && aligned(dst, 16)) return go(nearest_generic<BPP, 16>);
@@ -288,18 +288,21 @@ int linear_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
 
 template <int BPP, typename T, int C>
 int nearest_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                     hipStream_t st)
+                     int map, hipStream_t st)
 {
     const Path path = path_override();
     if constexpr (sizeof(T) == 1) {
-        if (path == Path::Auto && up2_path_fits(C, H, W, dH, dW, src, dst))
+        // an exact 2x enlargement replicates pixels under the half-pixel and
+        // the floor mapping alike (not under round, which shifts by one)
+        if (path == Path::Auto && map != kNearestRound && up2_path_fits(C, H, W, dH, dW, src, dst))
             return launch_up2_u8<C, true>(src, dst, batch, H, W, st);
     }
     int rc;
     const bool small = (long long)batch * dH * dW < kSmallOutPixels;
     if (path == Path::RowSeg || (path == Path::Auto && !small))
-        if (try_rowseg<T, C, true>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
-    return launch_nearest<BPP>(src, dst, batch, H, W, dH, dW, st);
+        if (try_rowseg<T, C, true>(src, dst, batch, H, W, dH, dW, st, rc, Affine{}, nullptr, map))
+            return rc;
+    return launch_nearest<BPP>(src, dst, batch, H, W, dH, dW, map, st);
 }
 
 template <int C, int OUT>
@@ -409,24 +412,35 @@ int resize_linear(const void *src, void *dst, int batch, int H, int W, int C, in
     }
 }
 
-int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
-                   int dst_H, int dst_W, void *stream)
+int resize_nearest_mapping(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                           int dst_H, int dst_W, int mapping, void *stream)
 {
     const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W);
     if (rc != MI_RESIZE_OK) return rc;
+    if (mapping != MI_RESIZE_NEAREST_HALF_PIXEL && mapping != MI_RESIZE_NEAREST_FLOOR &&
+        mapping != MI_RESIZE_NEAREST_ROUND)
+        return MI_RESIZE_ERR_PARAM;
     hipStream_t st = (hipStream_t)stream;
+    const int m = mapping;
     if (dtype == MI_RESIZE_U8) {
         switch (C) {
-        case 1: return nearest_dispatch<1, uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
-        case 3: return nearest_dispatch<3, uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
-        default: return nearest_dispatch<4, uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+        case 1: return nearest_dispatch<1, uint8_t, 1>(src, dst, batch, H, W, dst_H, dst_W, m, st);
+        case 3: return nearest_dispatch<3, uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, m, st);
+        default: return nearest_dispatch<4, uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, m, st);
         }
     }
     switch (C) {
-    case 1: return nearest_dispatch<4, float, 1>(src, dst, batch, H, W, dst_H, dst_W, st);
-    case 3: return nearest_dispatch<12, float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
-    default: return nearest_dispatch<16, float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+    case 1: return nearest_dispatch<4, float, 1>(src, dst, batch, H, W, dst_H, dst_W, m, st);
+    case 3: return nearest_dispatch<12, float, 3>(src, dst, batch, H, W, dst_H, dst_W, m, st);
+    default: return nearest_dispatch<16, float, 4>(src, dst, batch, H, W, dst_H, dst_W, m, st);
     }
+}
+
+int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                   int dst_H, int dst_W, void *stream)
+{
+    return resize_nearest_mapping(src, dst, batch, H, W, C, dtype, dst_H, dst_W,
+                                  MI_RESIZE_NEAREST_HALF_PIXEL, stream);
 }
 
 int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W, int C,

@@ -116,12 +116,27 @@ __device__ __forceinline__ float weightf(const Tap &t)
     return (float)t.r / (float)t.den;
 }
 
-// Nearest source index: the half-pixel coordinate rounded half up,
-// floor((2d + 1) n_in / (2 n_out)), limited to n_in - 1 (exact by the same
-// argument as axis_tap).
-__device__ __forceinline__ int nearest_index(int d, int n_in, int n_out)
+// Nearest source index under one of three mappings, each
+// floor((2 d n_in + bias) / (2 n_out)) limited to n_in - 1 and exact by the
+// same argument as axis_tap:
+//   kNearestHalfPixel  (the default) the half-pixel coordinate rounded half
+//                      up, floor((2d + 1) n_in / (2 n_out)): bias n_in;
+//   kNearestFloor      the corner-aligned coordinate d n_in / n_out
+//                      (hnwysp.cn news/129086 s3.2 maps d / scale with no
+//                      half-pixel shift), floored - the legacy nearest of
+//                      image libraries: bias 0;
+//   kNearestRound      the same coordinate rounded half up, as that kernel's
+//                      floor(x + 0.5): bias n_out.
+enum : int { kNearestHalfPixel = 0, kNearestFloor = 1, kNearestRound = 2 };
+
+__device__ __forceinline__ int nearest_bias(int map, int n_in, int n_out)
 {
-    const long long num = (long long)(2 * d + 1) * n_in;
+    return map == kNearestFloor ? 0 : (map == kNearestRound ? n_out : n_in);
+}
+
+__device__ __forceinline__ int nearest_index(int d, int n_in, int n_out, int map)
+{
+    const long long num = 2LL * d * n_in + nearest_bias(map, n_in, n_out);
     const long long den = 2LL * n_out;
     long long q = (long long)floor((double)num / (double)den);
     long long r = num - q * den;
@@ -544,7 +559,7 @@ template <> struct CopyUnit<16> { using type = uint4; };
 template <int BPP, int UNIT>
 __global__ __launch_bounds__(kBlock) void nearest_generic(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W, int dH, int dW,
-    long long rows_total, int rows_per_block, int col_blocks)
+    long long rows_total, int rows_per_block, int col_blocks, int map)
 {
     using U = typename CopyUnit<UNIT>::type;
     constexpr int K = BPP / UNIT;
@@ -552,7 +567,7 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
     const long long rb = blockIdx.x / (unsigned)col_blocks;
     const int x = cb * kBlock + (int)threadIdx.x;
     if (x >= dW) return;
-    const size_t sx = (size_t)nearest_index(x, W, dW) * BPP;
+    const size_t sx = (size_t)nearest_index(x, W, dW, map) * BPP;
 
     long long g = rb * rows_per_block;
     long long g_end = g + rows_per_block;
@@ -560,7 +575,7 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
     long long n = g / dH;
     int dy = (int)(g - n * dH);
     for (; g < g_end; ++g) {
-        const int sy = nearest_index(dy, H, dH);
+        const int sy = nearest_index(dy, H, dH, map);
         const U *from = (const U *)(src + (((size_t)n * H + sy) * W) * BPP + sx);
         U *to = (U *)(dst + ((size_t)g * dW + x) * BPP);
 #pragma unroll
@@ -788,10 +803,13 @@ struct AxisStepper {
     int q, r;              // floor and remainder of num / den for the current row
     int dq, dr;            // 2 n_in = dq * den + dr
     int den;
-    __device__ void init(int d, int n_in, int n_out)
+    __device__ void init(int d, int n_in, int n_out) { init_biased(d, n_in, n_out, n_in - n_out); }
+    // numerator 2 d n_in + bias instead of (2d + 1) n_in - n_out (nearest
+    // mappings; bias in [0, n_in + n_out])
+    __device__ void init_biased(int d, int n_in, int n_out, int bias)
     {
         den = 2 * n_out;
-        const long long num = (long long)(2 * d + 1) * n_in - n_out;
+        const long long num = 2LL * d * n_in + bias;
         long long q64 = (long long)floor((double)num / (double)den);
         long long r64 = num - q64 * den;
         if (r64 < 0) { q64 -= 1; r64 += den; } else if (r64 >= den) { q64 += 1; r64 -= den; }
@@ -851,7 +869,7 @@ template <typename T, int C, bool NEAREST, int KMAX, bool NT, int OUT = kOutSame
 __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff,
-    const int32_t *__restrict__ rois)
+    const int32_t *__restrict__ rois, int nn_map)
 {
     T *const dst = (T *)dst_v;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
@@ -895,8 +913,8 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             sa = min(a0, a1);
             sb = max(b0, b1);
         } else if constexpr (NEAREST) {
-            sa = nearest_index(wx0, c.w, dW);
-            sb = nearest_index(wx1, c.w, dW);
+            sa = nearest_index(wx0, c.w, dW, nn_map);
+            sb = nearest_index(wx1, c.w, dW, nn_map);
         } else {
             sa = axis_tap(wx0, c.w, dW).a;
             sb = axis_tap(wx1, c.w, dW).b;
@@ -915,14 +933,15 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     float twf[PX];
     auto lane_table = [&](const Crop &c, int sa) {
         AxisStepper xs;
-        xs.init(min(x0, dW - 1), c.w, dW);
+        // nearest steps its own mapping's numerator, whose floor is the index
+        xs.init_biased(min(x0, dW - 1), c.w, dW,
+                       NEAREST ? nearest_bias(nn_map, c.w, dW) : c.w - dW);
         const int last = c.w - 1;
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
             if (p > 0 && x0 + p <= dW - 1) xs.next();
             if constexpr (NEAREST) {
-                // floor((2x + 1) n_in / (2 n_out)) = floor((num + n_out) / den)
-                const int k = xs.q + ((xs.r + dW) >= xs.den ? 1 : 0);
+                const int k = xs.q;
                 toff[p] = (min(k, last) - sa) * PB;
                 tnext[p] = false;
                 tw[p] = 0;
@@ -974,7 +993,10 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     set_segment();
     lane_table(crop, seg_sa);
     AxisStepper ys;
-    ys.init(pdy, crop.h, dH);
+    auto row_init = [&](int d) {
+        ys.init_biased(d, crop.h, dH, NEAREST ? nearest_bias(nn_map, crop.h, dH) : crop.h - dH);
+    };
+    row_init(pdy);
     // global source row held in each LDS slot, and its offset there
     long long held0 = -1, held1 = -1;
     int mis0 = 0, mis1 = 0;
@@ -997,8 +1019,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             if constexpr (sizeof(T) == 1) P.wy1 = weight11(t);
             else P.wyf = weightf(t);
         } else if constexpr (NEAREST) {
-            // nearest row: floor((2dy + 1) H / (2 dH)) = floor((num + dH) / den)
-            const int k = ys.q + ((ys.r + dH) >= ys.den ? 1 : 0);
+            const int k = ys.q;          // the mapping's floor (non-negative)
             ya = yb = k > Hc - 1 ? Hc - 1 : (k < 0 ? 0 : k);
         } else {
             const int q = ys.q;
@@ -1048,7 +1069,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                 crop = load_crop(rois, pn, H, W);
                 set_segment();
             }
-            ys.init(0, crop.h, dH);
+            row_init(0);
         } else {
             ys.next();
         }

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MI_RESIZE_ABI_VERSION 4
+#define MI_RESIZE_ABI_VERSION 5
 
 enum mi_resize_dtype {
     MI_RESIZE_U8 = 0,   /* uint8_t elements  */
@@ -80,6 +80,12 @@ enum mi_resize_border {
     MI_RESIZE_BORDER_WRAP = 2     /* periodic image                                   */
 };
 
+enum mi_resize_nearest_mapping {
+    MI_RESIZE_NEAREST_HALF_PIXEL = 0,  /* pixel centres, rounded half up (resize_nearest) */
+    MI_RESIZE_NEAREST_FLOOR = 1,       /* corner-aligned d * W / dW, floored (legacy)      */
+    MI_RESIZE_NEAREST_ROUND = 2        /* corner-aligned d * W / dW, rounded half up       */
+};
+
 enum mi_resize_status {
     MI_RESIZE_OK = 0,
     MI_RESIZE_ERR_NULL = 1,      /* src or dst is NULL                        */
@@ -89,7 +95,7 @@ enum mi_resize_status {
     MI_RESIZE_ERR_OVERLAP = 5,   /* src and dst byte ranges overlap           */
     MI_RESIZE_ERR_HIP = 6,       /* the HIP runtime refused the launch        */
     MI_RESIZE_ERR_ALIGN = 7,     /* float32 src or dst not 4-byte aligned     */
-    MI_RESIZE_ERR_PARAM = 8      /* bad normalisation parameters              */
+    MI_RESIZE_ERR_PARAM = 8      /* bad parameter of an extended entry point  */
 };
 
 /* Linear (bilinear) resize; see the header comment for the exact result. */
@@ -99,6 +105,25 @@ int resize_linear(const void *src, void *dst, int batch, int H, int W, int C,
 /* Nearest-neighbour resize (half-pixel centres, rounding half up). */
 int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C,
                    int dtype, int dst_H, int dst_W, void *stream);
+
+/*
+ * Nearest-neighbour resize with a choice of coordinate mapping; per axis,
+ * output index d of dW (or dH) picks source index
+ *   MI_RESIZE_NEAREST_HALF_PIXEL  floor((d + 1/2) W / dW): identical to
+ *                                 resize_nearest;
+ *   MI_RESIZE_NEAREST_FLOOR       floor(d W / dW): the corner-aligned
+ *                                 coordinate d / scale of hnwysp.cn news/129086
+ *                                 s3.2 (scale = dW / W), floored - the legacy
+ *                                 nearest of image libraries;
+ *   MI_RESIZE_NEAREST_ROUND       floor(d W / dW + 1/2): the same coordinate
+ *                                 rounded half up, as that section's kernel
+ *                                 does;
+ * each limited to W - 1, all in exact integer arithmetic.  Elements are copied
+ * bit for bit.  Other arguments, layout and errors as resize_nearest; an
+ * unknown mapping returns MI_RESIZE_ERR_PARAM.
+ */
+int resize_nearest_mapping(const void *src, void *dst, int batch, int H, int W, int C,
+                           int dtype, int dst_H, int dst_W, int mapping, void *stream);
 
 /*
  * Linear resize fused with normalisation, for batches fed to a network.

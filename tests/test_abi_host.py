@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("resize_linear", "resize_nearest", "resize_status_string",
               "resize_abi_version", "resize_copy_bytes", "resize_linear_normalize",
-              "resize_linear_roi", "resize_linear_border"):
+              "resize_linear_roi", "resize_linear_border", "resize_nearest_mapping"):
         assert n in names
 
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert R.resize_abi_version() == 4
+    assert R.resize_abi_version() == 5
     for code in range(9):
         s = R.resize_status_string(code)
         assert isinstance(s, str) and s
@@ -133,3 +133,15 @@ def test_border_validation():
     assert lib.resize_linear_border(*args, 3, None) == 8
     assert lib.resize_linear_border(*args, -1, None) == 8
     assert lib.resize_linear_border(None, FAKE_DST, 1, 8, 8, 3, 0, 4, 4, 1, None) == 1
+
+
+def test_nearest_mapping_validation():
+    """Argument checks of resize_nearest_mapping run on the host before any
+    HIP call: an unknown mapping is a parameter error, and the common checks
+    still come first."""
+    lib = R._load()
+    args = (FAKE_SRC, FAKE_DST, 1, 8, 8, 3, 0, 4, 4)
+    assert lib.resize_nearest_mapping(*args, 3, None) == 8
+    assert lib.resize_nearest_mapping(*args, -1, None) == 8
+    assert lib.resize_nearest_mapping(None, FAKE_DST, 1, 8, 8, 3, 0, 4, 4, 1, None) == 1
+    assert lib.resize_nearest_mapping(FAKE_SRC, FAKE_DST, 1, 8, 8, 5, 0, 4, 4, 2, None) == 3

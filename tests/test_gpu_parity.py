@@ -485,3 +485,26 @@ def test_border_thumb_full_size(border):
     torch.cuda.synchronize()
     assert_parity(dst.cpu().numpy(), oracle.resize_linear(s, w.dH, w.dW, border=border),
                   "border %s thumb" % border)
+
+
+# --------------------------------------------------------------------------
+# nearest coordinate mappings (half_pixel, floor, round)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
+@pytest.mark.parametrize("mapping", ["half_pixel", "floor", "round"])
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_nearest_mappings(mapping, dtype, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
+    r = np.random.default_rng(818 + 3 * (dtype == "f32") + ["half_pixel", "floor", "round"].index(mapping))
+    shapes = [random_case(r) for _ in range(30)] + EDGE[:14] + [(1, 540, 960, 1, 1080, 1920),
+                                                                (2, 64, 96, 3, 128, 192)]
+    for i, (N, H, W, C, dH, dW) in enumerate(shapes):
+        say("case nearest %s %s %s #%d %s" % (mapping, dtype, path, i, (N, H, W, C, dH, dW)))
+        s = random_image(r, (N, H, W, C), dtype)
+        src = torch.from_numpy(s).cuda()
+        dst = torch.empty((N, dH, dW, C), dtype=src.dtype, device="cuda")
+        R.resize_nearest_mapping(src, dst, mapping=mapping)
+        torch.cuda.synchronize()
+        assert_parity(dst.cpu().numpy(), oracle.resize_nearest(s, dH, dW, mapping=mapping),
+                      "nearest %s #%d %s" % (mapping, i, (N, H, W, C, dH, dW)))
