@@ -143,6 +143,32 @@ def resize_linear_normalize(src: np.ndarray, dH: int, dW: int, alpha, mean, std,
     raise ValueError("layout must be NCHW or NHWC")
 
 
+def rgb_to_grey(src: np.ndarray) -> np.ndarray:
+    """Per-pixel grey value of an NHWC RGB(A) array (channels R, G, B first;
+    a fourth channel is ignored), with the luma weights of ITU-R BT.601,
+    0.299 R + 0.587 G + 0.114 B.  uint8: the exact value rounded half up,
+    (299 R + 587 G + 114 B + 500) // 1000.  float32: evaluated in float64 and
+    rounded to float32 once.  Returns N x H x W x 1 of the source dtype."""
+    src = _as_nhwc(src)
+    if src.shape[3] not in (3, 4):
+        raise ValueError("grey conversion needs 3 or 4 channels")
+    r, g, b = (src[..., k:k + 1] for k in range(3))
+    if src.dtype == np.uint8:
+        r, g, b = (v.astype(np.int64) for v in (r, g, b))
+        return ((299 * r + 587 * g + 114 * b + 500) // 1000).astype(np.uint8)
+    r, g, b = (v.astype(np.float64) for v in (r, g, b))
+    return (0.299 * r + 0.587 * g + 0.114 * b).astype(np.float32)
+
+
+def resize_linear_grey(src: np.ndarray, dH: int, dW: int) -> np.ndarray:
+    """RGB(A) -> grey, then linear resize of the grey image: the pages'
+    object-detection preprocessing runs cvtColor (RGB2Gray) before resize
+    ("Performance Optimization of Object Tracking Algorithms in OpenCV on
+    GPUs" s3.1.1), here fused into one pass.  The grey image is the exact
+    per-pixel conversion above; the resize is the pinned resize_linear."""
+    return resize_linear(rgb_to_grey(src), dH, dW)
+
+
 def clamp_roi(roi, H: int, W: int):
     """The crop {x, y, w, h} clamped into an H x W image: x to [0, W-1],
     w to [1, W - x], y and h likewise (the library's documented rule)."""

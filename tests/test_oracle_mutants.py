@@ -10,6 +10,7 @@ import os
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import oracle
@@ -80,3 +81,24 @@ def test_pins_catch_mutant(mutant, monkeypatch):
                 break
         monkeypatch.setattr(oracle, "_lib", None)
     assert caught is not None, "no pin fails for mutant %s" % mutant
+
+
+def _grey_swapped_rb(src):
+    src = oracle._as_nhwc(src)
+    r, g, b = (src[..., k:k + 1].astype(np.int64) for k in range(3))
+    return ((114 * r + 587 * g + 299 * b + 500) // 1000).astype(np.uint8)
+
+
+def _grey_truncated(src):
+    src = oracle._as_nhwc(src)
+    r, g, b = (src[..., k:k + 1].astype(np.int64) for k in range(3))
+    return ((299 * r + 587 * g + 114 * b) // 1000).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mutant", [_grey_swapped_rb, _grey_truncated])
+def test_grey_pins_catch_mutant(mutant, monkeypatch):
+    """The grey conversion lives in the Python half of the oracle: swap its
+    red and blue weights, or truncate instead of rounding, and its pins fail."""
+    monkeypatch.setattr(oracle, "rgb_to_grey", mutant)
+    with pytest.raises(AssertionError):
+        pins.test_grey_closed_forms()

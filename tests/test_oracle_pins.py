@@ -371,6 +371,38 @@ def test_nearest_round_brute_force():
 
 
 # --------------------------------------------------------------------------
+# fused RGB -> grey (BT.601 luma weights), then resize
+# --------------------------------------------------------------------------
+def test_grey_closed_forms():
+    """0.299 R + 0.587 G + 0.114 B, rounded half up: pure red 255 -> 76.245
+    -> 76, green -> 149.685 -> 150, blue -> 29.07 -> 29, white -> 255, any
+    grey v stays v, and the tie 114 * 250 / 1000 = 28.5 rounds up to 29."""
+    px = [((255, 0, 0), 76), ((0, 255, 0), 150), ((0, 0, 255), 29), ((255, 255, 255), 255),
+          ((0, 0, 250), 29), ((0, 0, 0), 0), ((1, 0, 0), 0), ((2, 0, 0), 1)]
+    src = np.array([[[p for p, _ in px]]], dtype=np.uint8)
+    assert oracle.rgb_to_grey(src)[0, 0, :, 0].tolist() == [v for _, v in px]
+    vals = np.arange(256, dtype=np.uint8)
+    greys = np.stack([vals, vals, vals], axis=-1)[None, None]
+    assert np.array_equal(oracle.rgb_to_grey(greys)[0, 0, :, 0], vals)
+    f = np.array([[[[1, 0, 0, 7], [0, 1, 0, 7], [0, 0, 1, 7], [0.5, 0.5, 0.5, 0]]]], np.float32)
+    assert np.allclose(oracle.rgb_to_grey(f)[0, 0, :, 0], [0.299, 0.587, 0.114, 0.5], atol=1e-7, rtol=0)
+
+
+def test_grey_ignores_alpha_and_resizes_as_grey_image():
+    """A fourth channel does not matter; at scale 1 the result is the grey
+    image itself; an exact 2:1 downscale is the rounded mean of the greys."""
+    r = rng(16)
+    s = rand_img(r, (2, 10, 12, 4), np.uint8)
+    s2 = s.copy()
+    s2[..., 3] = 255 - s2[..., 3]
+    assert np.array_equal(oracle.resize_linear_grey(s, 5, 6), oracle.resize_linear_grey(s2, 5, 6))
+    g = oracle.rgb_to_grey(s).astype(np.int64)
+    assert np.array_equal(oracle.resize_linear_grey(s, 10, 12), g.astype(np.uint8))
+    mean = (g[:, 0::2, 0::2] + g[:, 0::2, 1::2] + g[:, 1::2, 0::2] + g[:, 1::2, 1::2] + 2) >> 2
+    assert np.array_equal(oracle.resize_linear_grey(s, 5, 6), mean.astype(np.uint8))
+
+
+# --------------------------------------------------------------------------
 # layout invariants: transpose, horizontal flip, channels, batch
 # --------------------------------------------------------------------------
 def test_transpose_equivariance():
