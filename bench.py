@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="4k")
     p.add_argument("--mode", default=None, help="linear (default) or nearest")
-    p.add_argument("--op", default="resize", choices=["resize", "normalize", "crop"],
+    p.add_argument("--op", default="resize", choices=["resize", "normalize", "crop", "grey"],
                    help="normalize: the fused uint8 -> float32 NCHW resize + normalisation "
                         "(ImageNet mean / std, alpha 1/255) on the same workload; crop: "
                         "batched crop-then-resize with seeded random-resized-crop regions")
@@ -227,6 +227,7 @@ def main():
     src0 = torch.from_numpy(src_np).to(dev)
     fused = args.op == "normalize"
     cropped = args.op == "crop"
+    grey = args.op == "grey"
     crops_np = None
     if cropped:
         rng = np.random.default_rng(w.seed + 77)
@@ -245,6 +246,10 @@ def main():
         dst_shape = (w.batch, w.C, w.dH, w.dW)
         dst_bytes = w.dst_pixels * w.C * 4
         tdt_out = torch.float32
+    elif grey:
+        if w.C not in (3, 4) or mode != "linear":
+            sys.exit("--op grey needs an RGB(A) linear workload")
+        dst_shape, dst_bytes, tdt_out = (w.batch, w.dH, w.dW, 1), w.dst_pixels * w.itemsize, tdt
     else:
         dst_shape, dst_bytes, tdt_out = w.dst_shape, w.dst_bytes, tdt
     src_bytes = w.src_bytes
@@ -270,8 +275,10 @@ def main():
 
         def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
             return base(s_, d_, N_, H_, W_, C_, dH_, dW_, 1.0 / 255.0, mean_c, std_c, 1, sh_)
+    if grey:
+        entry = lib.resize_linear_grey
     if args.border != "clamp":
-        if mode != "linear" or fused or cropped:
+        if mode != "linear" or fused or cropped or grey:
             sys.exit("--border applies to the plain linear resize")
         border_entry = lib.resize_linear_border
         border_code = {"mirror": 1, "wrap": 2}[args.border]
@@ -385,6 +392,9 @@ def main():
         if cropped:
             ref = oracle.resize_linear_roi(src_np, crops_np, w.dH, w.dW)
             ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
+        elif grey:
+            ref = oracle.resize_linear_grey(src_np, w.dH, w.dW)
+            ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
         elif fused:
             ref = oracle.resize_linear_normalize(src_np, w.dH, w.dW, 1 / 255, (0.485, 0.456, 0.406, 0.5)[:w.C],
                                                  (0.229, 0.224, 0.225, 0.25)[:w.C], "NCHW")
@@ -398,7 +408,7 @@ def main():
         if not ok:
             sys.exit("bench output disagrees with the oracle")
 
-    traffic = (None if (fused or cropped or args.border != "clamp")
+    traffic = (None if (fused or cropped or grey or args.border != "clamp")
                else traffic_bytes(MEASURED_TRAFFIC.get((w.name, mode))))
     line = {
         "metric": "bilinear resize Gpix/s + HBM GB/s (% of peak), RGB u8 4K->1080p, 1 GPU",
@@ -417,6 +427,7 @@ def main():
             "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s%s" % (
                 w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode,
                 " + normalize to f32 NCHW" if fused else (" of random crops" if cropped else
+                " to grey" if grey else
                 ("" if args.border == "clamp" else ", %s border" % args.border))),
             "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
             "mode": mode, "cache": "warm (1 pair)" if args.warm else "cold (%d rotating pairs)" % pairs,

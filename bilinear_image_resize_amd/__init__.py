@@ -35,7 +35,7 @@ _LIB_PATH = os.path.join(_PKG, "libmi_resize.so")
 
 U8 = 0
 F32 = 1
-_ABI_VERSION = 5
+_ABI_VERSION = 6
 
 _lib = None
 
@@ -82,6 +82,8 @@ def _load():
     lib.resize_linear_border.restype = ci
     lib.resize_nearest_mapping.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, vp]
     lib.resize_nearest_mapping.restype = ci
+    lib.resize_linear_grey.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.resize_linear_grey.restype = ci
     if lib.resize_abi_version() != _ABI_VERSION:
         raise RuntimeError("libmi_resize.so ABI version %d, binding expects %d"
                            % (lib.resize_abi_version(), _ABI_VERSION))
@@ -261,6 +263,23 @@ def resize_nearest_mapping(src, dst, mapping="floor", stream=None):
                                         _stream_handle(stream, src.device))
     if rc != 0:
         raise ResizeError(rc, "resize_nearest_mapping")
+    return dst
+
+
+def resize_linear_grey(src, dst, stream=None):
+    """RGB(A) -> grey (BT.601 luma weights) fused with the linear resize:
+    ``src`` (N,) H x W x 3|4, ``dst`` (N,) dst_H x dst_W x 1, same dtype."""
+    N, H, W, C = _nhwc(src, "src")
+    N2, dH, dW, C2 = _nhwc(dst, "dst")
+    if N2 != N or C2 != 1 or src.dim() != dst.dim() or src.dtype != dst.dtype:
+        raise ValueError("src %s / dst %s mismatch (dst needs one channel)"
+                         % (tuple(src.shape), tuple(dst.shape)))
+    if src.device != dst.device:
+        raise ValueError("src and dst are on different devices")
+    rc = _load().resize_linear_grey(src.data_ptr(), dst.data_ptr(), N, H, W, C, _dtype_code(src),
+                                    dH, dW, _stream_handle(stream, src.device))
+    if rc != 0:
+        raise ResizeError(rc, "resize_linear_grey")
     return dst
 
 

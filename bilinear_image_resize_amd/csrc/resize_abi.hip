@@ -42,9 +42,11 @@ Path path_override()
     return Path::Auto;
 }
 
+// dC: channels of dst (C unless the output stage changes them)
 int check_args(const void *src, const void *dst, int batch, int H, int W, int C, int dtype,
-               int dH, int dW)
+               int dH, int dW, int dC = 0)
 {
+    if (dC == 0) dC = C;
     if (!src || !dst) return MI_RESIZE_ERR_NULL;
     if (dtype != MI_RESIZE_U8 && dtype != MI_RESIZE_F32) return MI_RESIZE_ERR_DTYPE;
     if (C != 1 && C != 3 && C != 4) return MI_RESIZE_ERR_CHANNELS;
@@ -55,7 +57,7 @@ int check_args(const void *src, const void *dst, int batch, int H, int W, int C,
     const size_t es = dtype == MI_RESIZE_U8 ? 1 : 4;
     const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
     const uintptr_t s1 = s0 + (size_t)batch * H * W * C * es;
-    const uintptr_t d1 = d0 + (size_t)batch * dH * dW * C * es;
+    const uintptr_t d1 = d0 + (size_t)batch * dH * dW * dC * es;
     if (s0 < d1 && d0 < s1) return MI_RESIZE_ERR_OVERLAP;
     if (es == 4 && (!aligned(src, 4) || !aligned(dst, 4))) return MI_RESIZE_ERR_ALIGN;
     return MI_RESIZE_OK;
@@ -114,13 +116,13 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
 
 constexpr long long kMaxGridY = 65535;
 
-template <int C>
+template <int C, bool GREY = false>
 int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStream_t st)
 {
     constexpr int seg = kHalfLanes * HalfShape<C>::PX;
     const long long rows = (long long)batch * dH;
     const dim3 grid((dW + seg - 1) / seg, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
-    return launch(linear_half_u8<C>, grid, dim3(kHalfLanes), 0, st, (const uint8_t *)src,
+    return launch(linear_half_u8<C, GREY>, grid, dim3(kHalfLanes), 0, st, (const uint8_t *)src,
                   (uint8_t *)dst, dW, rows);
 }
 
@@ -366,6 +368,26 @@ int border_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
     return go(linear_generic<T, C, false, kOutSame, false, kBorderWrap>);
 }
 
+template <typename T, int C>
+int grey_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                  hipStream_t st)
+{
+    const long long rows = (long long)batch * dH;
+    const Path path = path_override();
+    if constexpr (sizeof(T) == 1) {
+        if (path == Path::Auto && half_path_fits(C, H, W, dH, dW, src, dst))
+            return launch_half_u8<C, true>(src, dst, batch, dH, dW, st);
+    }
+    const bool small = rows * dW < kSmallOutPixels;
+    int rc;
+    if (path == Path::RowSeg || (path == Path::Auto && !small))
+        if (try_rowseg<T, C, false, kOutGrey>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
+    const Grid g = band_grid(rows, dW);
+    return launch(linear_generic<T, C, false, kOutGrey>, dim3(g.blocks), dim3(kBlock), 0, st,
+                  (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks,
+                  Affine{}, (const int32_t *)nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,6 +456,21 @@ int resize_nearest_mapping(const void *src, void *dst, int batch, int H, int W, 
     case 3: return nearest_dispatch<12, float, 3>(src, dst, batch, H, W, dst_H, dst_W, m, st);
     default: return nearest_dispatch<16, float, 4>(src, dst, batch, H, W, dst_H, dst_W, m, st);
     }
+}
+
+int resize_linear_grey(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                       int dst_H, int dst_W, void *stream)
+{
+    const int rc = check_args(src, dst, batch, H, W, C, dtype, dst_H, dst_W, 1);
+    if (rc != MI_RESIZE_OK) return rc;
+    if (C != 3 && C != 4) return MI_RESIZE_ERR_CHANNELS;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == MI_RESIZE_U8) {
+        if (C == 3) return grey_dispatch<uint8_t, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+        return grey_dispatch<uint8_t, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
+    }
+    if (C == 3) return grey_dispatch<float, 3>(src, dst, batch, H, W, dst_H, dst_W, st);
+    return grey_dispatch<float, 4>(src, dst, batch, H, W, dst_H, dst_W, st);
 }
 
 int resize_nearest(const void *src, void *dst, int batch, int H, int W, int C, int dtype,

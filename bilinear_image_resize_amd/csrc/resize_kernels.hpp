@@ -171,8 +171,25 @@ __device__ __forceinline__ float blend_f32(float p00, float p01, float p10, floa
 // where v is the exact uint8 resize result, either interleaved like the
 // source (NHWC) or as one plane per channel (NCHW).  The host derives
 // scale = alpha / std and bias = -mean / std in double precision.
+// kOutGrey (RGB or RGBA sources) converts every tap to grey first - the
+// pages' preprocessing runs cvtColor's RGB2Gray before resize ("Performance
+// Optimization of Object Tracking Algorithms in OpenCV on GPUs" s3.1.1) -
+// and stores one channel of the source type.
 // --------------------------------------------------------------------------
-enum : int { kOutSame = 0, kOutNormNHWC = 1, kOutNormNCHW = 2 };
+enum : int { kOutSame = 0, kOutNormNHWC = 1, kOutNormNCHW = 2, kOutGrey = 3 };
+
+// Grey value of one RGB pixel with the ITU-R BT.601 luma weights 0.299,
+// 0.587 and 0.114: exact for uint8, rounded half up; two fused
+// multiply-adds for float32.
+__device__ __forceinline__ unsigned grey_u8(unsigned r, unsigned g, unsigned b)
+{
+    return (299u * r + 587u * g + 114u * b + 500u) / 1000u;
+}
+
+__device__ __forceinline__ float grey_f32(float r, float g, float b)
+{
+    return fmaf(0.114f, b, fmaf(0.587f, g, 0.299f * r));
+}
 
 struct Affine {
     float scale[4];
@@ -267,6 +284,10 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                 for (int k = 0; k < C; ++k)
                     out[k] = (uint8_t)blend_u8(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k],
                                                wx1, wy1);
+            } else if constexpr (OUT == kOutGrey) {
+                auto gr = [](const T *p) { return grey_u8(p[0], p[1], p[2]); };
+                dst[(size_t)g * dW + x] =
+                    (uint8_t)blend_u8(gr(r0 + xa), gr(r0 + xb), gr(r1 + xa), gr(r1 + xb), wx1, wy1);
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
@@ -292,6 +313,10 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                 o.z = blend_f32(a.z, b.z, c.z, d.z, wxf, wyf);
                 o.w = blend_f32(a.w, b.w, c.w, d.w, wxf, wyf);
                 *(float4 *)out = o;
+            } else if constexpr (OUT == kOutGrey) {
+                auto gr = [](const T *p) { return grey_f32(p[0], p[1], p[2]); };
+                dst[(size_t)g * dW + x] =
+                    blend_f32(gr(r0 + xa), gr(r0 + xb), gr(r1 + xa), gr(r1 + xb), wxf, wyf);
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k)
@@ -344,16 +369,21 @@ __device__ __forceinline__ uint4 load_stream(const uint8_t *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int C>
+// GREY (C = 3 or 4): each source pixel is converted to grey first and one
+// byte per output pixel is stored; the 2:1 weights make the result the
+// rounded mean of the four greys, as the general formula gives.
+template <int C, bool GREY = false>
 __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows)
 {
+    static_assert(!GREY || C >= 3, "grey needs RGB(A)");
     constexpr int PX = HalfShape<C>::PX;
     constexpr int SEG = kHalfLanes * PX;          // output pixels per segment
     constexpr int SRC_B = 2 * SEG * C;            // source bytes per row per segment
     constexpr int NL = (SRC_B / 16 + kHalfLanes - 1) / kHalfLanes;   // loads per lane per row
     constexpr int LB = 2 * PX * C;                // source bytes per lane per row
-    constexpr int OB = PX * C;                    // output bytes per lane
+    constexpr int OC = GREY ? 1 : C;              // output channels
+    constexpr int OB = PX * OC;                   // output bytes per lane
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SRC_B];
 
     const int lane = threadIdx.x;
@@ -361,7 +391,7 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     const int seg_px = min(SEG, dW - seg * SEG);
     const int n16 = seg_px * 2 * C / 16;          // whole: dW meets the divisibility rule
     const size_t src_row = (size_t)2 * dW * C;
-    const size_t dst_row = (size_t)dW * C;
+    const size_t dst_row = (size_t)dW * OC;
     for (long long g = blockIdx.y; g < rows; g += gridDim.y) {
         const uint8_t *s0 = src + (size_t)(2 * g) * src_row + (size_t)seg * SRC_B;
         const uint8_t *s1 = s0 + src_row;
@@ -388,12 +418,24 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
             __builtin_memcpy(a, lds + LB * lane, LB);
             __builtin_memcpy(b, lds + SRC_B + LB * lane, LB);
             uint8_t r[OB];
+            if constexpr (GREY) {
 #pragma unroll
-            for (int k = 0; k < OB; ++k) {
-                const int p = 2 * k - k % C;      // first source byte of output byte k
-                r[k] = (uint8_t)(((unsigned)a[p] + a[p + C] + b[p] + b[p + C] + 2u) >> 2);
+                for (int k = 0; k < PX; ++k) {
+                    const int p = 2 * k * C;      // first byte of source pixel 2k
+                    const unsigned s4 = grey_u8(a[p], a[p + 1], a[p + 2]) +
+                                        grey_u8(a[p + C], a[p + C + 1], a[p + C + 2]) +
+                                        grey_u8(b[p], b[p + 1], b[p + 2]) +
+                                        grey_u8(b[p + C], b[p + C + 1], b[p + C + 2]);
+                    r[k] = (uint8_t)((s4 + 2u) >> 2);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < OB; ++k) {
+                    const int p = 2 * k - k % C;  // first source byte of output byte k
+                    r[k] = (uint8_t)(((unsigned)a[p] + a[p + C] + b[p] + b[p + C] + 2u) >> 2);
+                }
             }
-            uint8_t *o = dst + (size_t)g * dst_row + (size_t)seg * SEG * C + (size_t)lane * OB;
+            uint8_t *o = dst + (size_t)g * dst_row + (size_t)seg * SEG * OC + (size_t)lane * OB;
             if constexpr (OB % 16 == 0) {
 #pragma unroll
                 for (int k = 0; k < OB / 16; ++k) {
@@ -877,6 +919,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     constexpr int PB = C * (int)sizeof(T);        // bytes per pixel
     static_assert(B == kBorderClamp || (!NEAREST && !ROI && OUT == kOutSame),
                   "mirror / wrap borders are for the plain linear resize");
+    static_assert(OUT != kOutGrey || (!NEAREST && C >= 3), "grey needs a linear RGB(A) resize");
     // Wrap stages each row with a one-pixel halo: column -1 (= W - 1) in
     // front of it, column W (= 0) behind it.  PAD bytes in front of the
     // staged chunks hold the first; the slot's slack the second.
@@ -1133,6 +1176,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         }
 
         T res[PX * C];
+        T resg[PX];                   // kOutGrey: one grey value per pixel
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
             if constexpr (NEAREST) {
@@ -1175,11 +1219,18 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                                                  : b_lo;
                     const uint32_t a2w = (C == 4 && tnext[p]) ? a_hi : a2;
                     const uint32_t b2w = (C == 4 && tnext[p]) ? b_hi : b2;
+                    if constexpr (OUT == kOutGrey) {
+                        auto gr = [](uint32_t w) {
+                            return grey_u8(w & 255u, (w >> 8) & 255u, (w >> 16) & 255u);
+                        };
+                        resg[p] = (T)blend_u8(gr(a_lo), gr(a2w), gr(b_lo), gr(b2w), tw[p], wy1);
+                    } else {
 #pragma unroll
-                    for (int c = 0; c < C; ++c) {
-                        const unsigned p00 = (a_lo >> (8 * c)) & 255u, p01 = (a2w >> (8 * c)) & 255u;
-                        const unsigned p10 = (b_lo >> (8 * c)) & 255u, p11 = (b2w >> (8 * c)) & 255u;
-                        res[p * C + c] = (T)blend_u8(p00, p01, p10, p11, tw[p], wy1);
+                        for (int c = 0; c < C; ++c) {
+                            const unsigned p00 = (a_lo >> (8 * c)) & 255u, p01 = (a2w >> (8 * c)) & 255u;
+                            const unsigned p10 = (b_lo >> (8 * c)) & 255u, p11 = (b2w >> (8 * c)) & 255u;
+                            res[p * C + c] = (T)blend_u8(p00, p01, p10, p11, tw[p], wy1);
+                        }
                     }
                 } else {
                     // float taps sit at 4-byte aligned LDS addresses (the
@@ -1195,11 +1246,19 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                         __builtin_memcpy(ra2, __builtin_assume_aligned(la + toff[p], 4), 2 * PB);
                         __builtin_memcpy(rb2, __builtin_assume_aligned(lb + toff[p], 4), 2 * PB);
                     }
+                    if constexpr (OUT == kOutGrey) {
+                        const float a0 = grey_f32(ra2[0], ra2[1], ra2[2]);
+                        const float b0 = grey_f32(rb2[0], rb2[1], rb2[2]);
+                        const float a1 = tnext[p] ? grey_f32(ra2[C], ra2[C + 1], ra2[C + 2]) : a0;
+                        const float b1 = tnext[p] ? grey_f32(rb2[C], rb2[C + 1], rb2[C + 2]) : b0;
+                        resg[p] = blend_f32(a0, a1, b0, b1, twf[p], wyf);
+                    } else {
 #pragma unroll
-                    for (int c = 0; c < C; ++c) {
-                        const T a0 = ra2[c], a1 = tnext[p] ? ra2[C + c] : ra2[c];
-                        const T b0 = rb2[c], b1 = tnext[p] ? rb2[C + c] : rb2[c];
-                        res[p * C + c] = blend_f32(a0, a1, b0, b1, twf[p], wyf);
+                        for (int c = 0; c < C; ++c) {
+                            const T a0 = ra2[c], a1 = tnext[p] ? ra2[C + c] : ra2[c];
+                            const T b0 = rb2[c], b1 = tnext[p] ? rb2[C + c] : rb2[c];
+                            res[p * C + c] = blend_f32(a0, a1, b0, b1, twf[p], wyf);
+                        }
                     }
                 }
             }
@@ -1207,6 +1266,8 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         if (valid_px > 0) {
             if constexpr (OUT == kOutSame) {
                 store_chunk<T, PX * C>(out_lane + (size_t)g * dW * C, res, valid_px * C);
+            } else if constexpr (OUT == kOutGrey) {
+                store_chunk<T, PX>(dst + (size_t)g * dW + x0, resg, valid_px);
             } else {
                 float f[PX * C];
 #pragma unroll

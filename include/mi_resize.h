@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MI_RESIZE_ABI_VERSION 5
+#define MI_RESIZE_ABI_VERSION 6
 
 enum mi_resize_dtype {
     MI_RESIZE_U8 = 0,   /* uint8_t elements  */
@@ -185,6 +185,23 @@ int resize_linear_roi(const void *src, void *dst, int batch, int H, int W, int C
  */
 int resize_linear_border(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
                          int dst_H, int dst_W, int border, void *stream);
+
+/*
+ * Linear resize fused with the RGB -> grey conversion that precedes it in
+ * the pages' object-detection preprocessing (cvtColor's RGB2Gray, then
+ * resize: "Performance Optimization of Object Tracking Algorithms in OpenCV
+ * on GPUs" s3.1.1; kernels merged as in its s4).  Every source pixel becomes
+ *     grey = 0.299 R + 0.587 G + 0.114 B      (ITU-R BT.601 luma weights)
+ * - for uint8 exactly, rounded half up: (299 R + 587 G + 114 B + 500) / 1000;
+ * for float32 as two fused multiply-adds - and the grey image is resized
+ * exactly as resize_linear would resize it.
+ *
+ * src: batch x H x W x C with C = 3 (R, G, B) or 4 (R, G, B, alpha; alpha
+ * ignored).  dst: batch x dst_H x dst_W x 1, same dtype.  Errors as
+ * resize_linear; C other than 3 or 4 returns MI_RESIZE_ERR_CHANNELS.
+ */
+int resize_linear_grey(const void *src, void *dst, int batch, int H, int W, int C, int dtype,
+                       int dst_H, int dst_W, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *resize_status_string(int status);

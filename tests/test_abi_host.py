@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("resize_linear", "resize_nearest", "resize_status_string",
               "resize_abi_version", "resize_copy_bytes", "resize_linear_normalize",
-              "resize_linear_roi", "resize_linear_border", "resize_nearest_mapping"):
+              "resize_linear_roi", "resize_linear_border", "resize_nearest_mapping",
+              "resize_linear_grey"):
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert R.resize_abi_version() == 5
+    assert R.resize_abi_version() == 6
     for code in range(9):
         s = R.resize_status_string(code)
         assert isinstance(s, str) and s
@@ -145,3 +146,15 @@ def test_nearest_mapping_validation():
     assert lib.resize_nearest_mapping(*args, -1, None) == 8
     assert lib.resize_nearest_mapping(None, FAKE_DST, 1, 8, 8, 3, 0, 4, 4, 1, None) == 1
     assert lib.resize_nearest_mapping(FAKE_SRC, FAKE_DST, 1, 8, 8, 5, 0, 4, 4, 2, None) == 3
+
+
+def test_grey_validation():
+    """resize_linear_grey takes 3 or 4 source channels and checks overlap
+    against its one-channel destination."""
+    lib = R._load()
+    assert lib.resize_linear_grey(FAKE_SRC, FAKE_DST, 1, 8, 8, 1, 0, 4, 4, None) == 3
+    assert lib.resize_linear_grey(None, FAKE_DST, 1, 8, 8, 3, 0, 4, 4, None) == 1
+    assert lib.resize_linear_grey(FAKE_SRC, FAKE_DST, 1, 8, 8, 3, 2, 4, 4, None) == 4
+    assert lib.resize_linear_grey(FAKE_SRC, FAKE_DST, 1, 0, 8, 3, 0, 4, 4, None) == 2
+    # dst starting 16 bytes after src: 8x8x3 src bytes overlap it
+    assert lib.resize_linear_grey(FAKE_SRC, FAKE_SRC + 16, 1, 8, 8, 3, 0, 4, 4, None) == 5

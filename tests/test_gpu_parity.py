@@ -508,3 +508,55 @@ def test_nearest_mappings(mapping, dtype, path, monkeypatch):
         torch.cuda.synchronize()
         assert_parity(dst.cpu().numpy(), oracle.resize_nearest(s, dH, dW, mapping=mapping),
                       "nearest %s #%d %s" % (mapping, i, (N, H, W, C, dH, dW)))
+
+
+# --------------------------------------------------------------------------
+# fused RGB(A) -> grey + linear resize
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_grey_random_shapes(dtype, path, monkeypatch):
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
+    r = np.random.default_rng(919 + (dtype == "f32"))
+    shapes = []
+    for _ in range(30):
+        N, H, W, C, dH, dW = random_case(r)
+        shapes.append((N, H, W, 3 + (C == 4), dH, dW))
+    shapes += [(1, 1, 1, 3, 1, 1), (1, 1, 7, 4, 5, 1), (2, 33, 65, 3, 17, 129), (1, 600, 600, 4, 2, 3),
+               (2, 64, 128, 3, 32, 64), (1, 48, 96, 4, 24, 48), (3, 20, 1040, 3, 10, 520)]   # exact 2:1
+    for i, (N, H, W, C, dH, dW) in enumerate(shapes):
+        say("case grey %s %s #%d %s" % (dtype, path, i, (N, H, W, C, dH, dW)))
+        s = random_image(r, (N, H, W, C), dtype)
+        src = torch.from_numpy(s).cuda()
+        dst = torch.empty((N, dH, dW, 1), dtype=src.dtype, device="cuda")
+        R.resize_linear_grey(src, dst)
+        torch.cuda.synchronize()
+        assert_parity(dst.cpu().numpy(), oracle.resize_linear_grey(s, dH, dW),
+                      "grey %s #%d %s" % (dtype, i, (N, H, W, C, dH, dW)))
+
+
+def test_grey_thumb_full_size():
+    """The thumbnail batch (256 x 480x640x3 -> 224x224) to grey, in the launch
+    configuration the benchmark times; every image compared."""
+    w = WORKLOADS["thumb"]
+    say("case grey full size %s -> %dx%d" % (w.src_shape, w.dH, w.dW))
+    s = make_source(w)
+    src = torch.from_numpy(s).cuda()
+    dst = torch.empty((w.batch, w.dH, w.dW, 1), dtype=src.dtype, device="cuda")
+    R.resize_linear_grey(src, dst)
+    torch.cuda.synchronize()
+    assert_parity(dst.cpu().numpy(), oracle.resize_linear_grey(s, w.dH, w.dW), "grey thumb")
+
+
+def test_grey_4k_full_size():
+    """The 4K RGB frame to grey 1080p (exact 2:1: the rounded mean of the four
+    source greys), in the launch configuration a benchmark of it times."""
+    w = WORKLOADS["4k"]
+    say("case grey full size %s -> %dx%d" % (w.src_shape, w.dH, w.dW))
+    s = make_source(w)
+    src = torch.from_numpy(s).cuda()
+    dst = torch.empty((w.batch, w.dH, w.dW, 1), dtype=src.dtype, device="cuda")
+    R.resize_linear_grey(src, dst)
+    torch.cuda.synchronize()
+    assert_parity(dst.cpu().numpy(), oracle.resize_linear_grey(s, w.dH, w.dW), "grey 4k")
