@@ -146,11 +146,17 @@ __device__ __forceinline__ int nearest_index(int d, int n_in, int n_out, int map
 }
 
 // 11-bit fixed-point blend of one channel, exact in 32 bits:
-// every partial sum is below 2048 * 2048 * 255 + 2^21 < 2^31.
+// every partial sum is below 2048 * 2048 * 255 + 2^21 < 2^31.  The weights
+// lie in [0, 2048]; masking them to 12 bits (a no-op on their values, and
+// hoisted out of the row loop) shows the compiler that every product fits
+// the full-rate 24-bit multiply-add, where it otherwise picks quarter-rate
+// 32-bit multiplies and 64-bit multiply-adds.
 __device__ __forceinline__ unsigned blend_u8(unsigned p00, unsigned p01, unsigned p10,
                                              unsigned p11, unsigned wx1, unsigned wy1)
 {
-    const unsigned wx0 = 2048u - wx1, wy0 = 2048u - wy1;
+    wx1 &= 0xfffu;
+    wy1 &= 0xfffu;
+    const unsigned wx0 = (2048u - wx1) & 0xfffu, wy0 = (2048u - wy1) & 0xfffu;
     const unsigned top = __umul24(wx0, p00) + __umul24(wx1, p01);
     const unsigned bot = __umul24(wx0, p10) + __umul24(wx1, p11);
     return (__umul24(wy0, top) + __umul24(wy1, bot) + (1u << 21)) >> 22;
