@@ -557,8 +557,8 @@ __global__ __launch_bounds__(64) void linear_up2_u8(
 // --------------------------------------------------------------------------
 template <int C>
 __global__ __launch_bounds__(64) void nearest_up2_u8(
-    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
-    long long rows, int chunks_per_row)
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int /* H: unused, the
+    argument list matches linear_up2_u8 */, int W, long long rows, int chunks_per_row)
 {
     constexpr int S = Up2Shape<C>::S;
     constexpr int IN = S * C;
