@@ -578,8 +578,12 @@ int resize_copy_bytes(const void *src, void *dst, int64_t nbytes, void *stream)
     if (aligned(src, 16) && aligned(dst, 16)) {
         const long long n16 = nbytes / 16;
         if (n16 > 0) {
+            // up to 32 MiB one chunk per lane (more waves for a short
+            // launch); beyond, enough lanes for about one unrolled pass each
             long long blocks = (n16 + kBlock - 1) / kBlock;
-            if (blocks > 256 * 32) blocks = 256 * 32;
+            if (blocks > 8192)
+                blocks = (n16 + kBlock * kCopyUnroll - 1) / (kBlock * kCopyUnroll);
+            if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
             const int rc = launch(copy_16, dim3((unsigned)blocks), dim3(kBlock), 0, st,
                                   (const uint4 *)src, (uint4 *)dst, n16);
             if (rc != MI_RESIZE_OK) return rc;

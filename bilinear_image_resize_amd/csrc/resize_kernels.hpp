@@ -1304,15 +1304,28 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
 }
 
 // --------------------------------------------------------------------------
-// Plain copy (16-byte units, grid-stride) for bandwidth calibration, and a
-// byte copy for a ragged tail.
+// Plain copy for bandwidth calibration: 16-byte units, grid-stride, each lane
+// keeping kCopyUnroll loads in flight before it stores them (one load then
+// one store per pass would wait a full memory latency per chunk), with the
+// streaming hints a one-pass copy wants.  A byte copy covers a ragged tail.
 // --------------------------------------------------------------------------
+constexpr int kCopyUnroll = 4;
+
 __global__ __launch_bounds__(kBlock) void copy_16(const uint4 *__restrict__ src,
                                                   uint4 *__restrict__ dst, long long n16)
 {
+    const u32x4_t *s = (const u32x4_t *)src;
+    u32x4_t *d = (u32x4_t *)dst;
     const long long stride = (long long)gridDim.x * kBlock;
-    for (long long i = (long long)blockIdx.x * kBlock + threadIdx.x; i < n16; i += stride)
-        dst[i] = src[i];
+    long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+    for (; i + (kCopyUnroll - 1) * stride < n16; i += kCopyUnroll * stride) {
+        u32x4_t v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(s + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], d + i + u * stride);
+    }
+    for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
 __global__ __launch_bounds__(kBlock) void copy_1(const uint8_t *__restrict__ src,
