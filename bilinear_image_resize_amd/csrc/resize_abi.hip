@@ -231,15 +231,20 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
 template <int C, bool NEAREST>
 int launch_up2_u8(const void *src, void *dst, int batch, int H, int W, hipStream_t st)
 {
-    const int chunks_per_row = W / Up2Shape<C>::S;
-    const long long rows = (long long)batch * H;
-    const dim3 grid((chunks_per_row + 63) / 64, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
-    if constexpr (NEAREST)
+    const int chunks_per_row = W / (NEAREST ? Up2Shape<C>::S : Up2LinShape<C>::S);
+    if constexpr (NEAREST) {
+        const long long rows = (long long)batch * H;
+        const dim3 grid((chunks_per_row + 63) / 64, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
         return launch(nearest_up2_u8<C>, grid, dim3(64), 0, st, (const uint8_t *)src,
                       (uint8_t *)dst, H, W, rows, chunks_per_row);
-    else
+    } else {
+        // H <= 65535 by the argument limits; images beyond the grid's z
+        // extent are strided
+        const dim3 grid((chunks_per_row + 63) / 64, (unsigned)H,
+                        (unsigned)(batch < kMaxGridY ? batch : kMaxGridY));
         return launch(linear_up2_u8<C>, grid, dim3(64), 0, st, (const uint8_t *)src,
-                      (uint8_t *)dst, H, W, rows, chunks_per_row);
+                      (uint8_t *)dst, H, W, batch, chunks_per_row);
+    }
 }
 
 // Exact 2x uint8 upscale whose rows split into whole, 16-byte aligned lanes.

@@ -475,28 +475,94 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
 // rows j - 1, j, j + 1 (clamped) over pixels -1 .. S (the outer two clamped),
 // forms the horizontal 1:3 / 3:1 sums per row, then the vertical ones.
 // Needs W % S == 0, W * C % 16 == 0 and 16-byte aligned buffers.
-// Grid: x = 64-lane workgroups across a row, y = source rows (stride
-// gridDim.y) of the flattened N * H rows.
+// Grid: x = 64-lane workgroups across a row, y = source row j of an image,
+// z = image (stride gridDim.z), so no lane divides to find its image.
 // --------------------------------------------------------------------------
 template <int C> struct Up2Shape { static constexpr int S = C == 4 ? 8 : 16; };
+// source pixels per lane of the linear kernel: its own (smaller) chunks put
+// more waves on a frame than the nearest kernel needs
+template <int C> struct Up2LinShape { static constexpr int S = C == 4 ? 4 : 8; };
 
 template <int C>
 __global__ __launch_bounds__(64) void linear_up2_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
-    long long rows, int chunks_per_row)
+    int batch, int chunks_per_row)
 {
-    constexpr int S = Up2Shape<C>::S;
-    constexpr int IN = S * C;              // bytes of one source row chunk (multiple of 16)
-    constexpr int OUT = 2 * S * C;         // bytes of one output row chunk
+    constexpr int S = Up2LinShape<C>::S;
+    constexpr int IN = S * C;              // bytes of one source row chunk (multiple of 8)
+    constexpr int OUT = 2 * S * C;         // bytes of one output row chunk (multiple of 16)
+    static_assert(IN % 8 == 0 && OUT % 16 == 0, "chunk shape");
     const int m = blockIdx.x * 64 + threadIdx.x;
     if (m >= chunks_per_row) return;
     const size_t row_bytes = (size_t)W * C;
     const int x0 = m * S;                                  // first source pixel of the chunk
     const int xl = x0 > 0 ? x0 - 1 : 0;                    // left neighbour (clamped)
     const int xr = x0 + S < W ? x0 + S : W - 1;            // right neighbour (clamped)
-    for (long long t = blockIdx.y; t < rows; t += gridDim.y) {
-        const long long n = t / H;
-        const int j = (int)(t - n * H);
+    const int j = blockIdx.y;
+    if constexpr (C == 1) {
+        // Packed form: pairs of neighbouring bytes sit in the two 16-bit
+        // halves of a register (all sums stay below 4096, exact in 16 bits).
+        // For source pair k (bytes 2k, 2k + 1 of the chunk) and one source
+        // row: A = the left neighbours, B = the pair itself, R = the right
+        // neighbours; even outputs A + 3B, odd outputs 3B + R.
+        static_assert(S == 8, "the packed form below is written for 8-byte chunks");
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        auto pair = [](uint32_t hi, uint32_t lo, uint32_t sel) {
+            return __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(hi, lo, sel));
+        };
+        const int jr[3] = {j > 0 ? j - 1 : 0, j, j + 1 < H ? j + 1 : H - 1};
+        for (int n = blockIdx.z; n < batch; n += gridDim.z) {
+            const uint8_t *img = src + (size_t)n * H * row_bytes;
+            u16x2 hE[3][S / 2], hO[3][S / 2];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const uint8_t *row = img + (size_t)jr[r] * row_bytes;
+                uint2 w;
+                __builtin_memcpy(&w, __builtin_assume_aligned(row + x0, 8), 8);
+                const uint32_t lw = row[xl], rw = row[xr];
+                // bytes 0-3 of {hi:lo} are lo's, 4-7 hi's; 0x0c gives a zero byte
+                u16x2 Bv[4], Rv[4];
+                Bv[0] = pair(w.y, w.x, 0x0c010c00u);
+                Bv[1] = pair(w.y, w.x, 0x0c030c02u);
+                Bv[2] = pair(w.y, w.x, 0x0c050c04u);
+                Bv[3] = pair(w.y, w.x, 0x0c070c06u);
+                Rv[0] = pair(w.y, w.x, 0x0c020c01u);
+                Rv[1] = pair(w.y, w.x, 0x0c040c03u);
+                Rv[2] = pair(w.y, w.x, 0x0c060c05u);
+                Rv[3] = pair(rw, w.y, 0x0c040c03u);
+                const u16x2 A0 = pair(w.x, lw, 0x0c040c00u);
+#pragma unroll
+                for (int k = 0; k < S / 2; ++k) {
+                    const u16x2 Av = k == 0 ? A0 : Rv[k - 1];
+                    const u16x2 b3 = Bv[k] * (unsigned short)3;
+                    hE[r][k] = Av + b3;
+                    hO[r][k] = b3 + Rv[k];
+                }
+            }
+            uint32_t o0[S / 2], o1[S / 2];
+#pragma unroll
+            for (int k = 0; k < S / 2; ++k) {
+                const u16x2 tE = hE[1][k] * (unsigned short)3 + (unsigned short)8;
+                const u16x2 tO = hO[1][k] * (unsigned short)3 + (unsigned short)8;
+                const u16x2 e0 = (tE + hE[0][k]) >> (unsigned short)4, e1 = (tE + hE[2][k]) >> (unsigned short)4;
+                const u16x2 d0 = (tO + hO[0][k]) >> (unsigned short)4, d1 = (tO + hO[2][k]) >> (unsigned short)4;
+                // output bytes E[2k], O[2k], E[2k+1], O[2k+1]
+                o0[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d0),
+                                              __builtin_bit_cast(uint32_t, e0), 0x06020400u);
+                o1[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d1),
+                                              __builtin_bit_cast(uint32_t, e1), 0x06020400u);
+            }
+            uint8_t *d0p = dst + ((size_t)n * 2 * H + 2 * j) * (2 * row_bytes) + (size_t)x0 * 2;
+            uint8_t *d1p = d0p + 2 * row_bytes;
+#pragma unroll
+            for (int k = 0; k < OUT / 16; ++k) {
+                ((uint4 *)d0p)[k] = make_uint4(o0[4 * k], o0[4 * k + 1], o0[4 * k + 2], o0[4 * k + 3]);
+                ((uint4 *)d1p)[k] = make_uint4(o1[4 * k], o1[4 * k + 1], o1[4 * k + 2], o1[4 * k + 3]);
+            }
+        }
+        return;
+    }
+    for (int n = blockIdx.z; n < batch; n += gridDim.z) {
         const uint8_t *img = src + (size_t)n * H * row_bytes;
         const int jr[3] = {j > 0 ? j - 1 : 0, j, j + 1 < H ? j + 1 : H - 1};
         // px[r][i]: row r, pixel i - 1 (i = 0 .. S + 1), channel-interleaved bytes
@@ -504,10 +570,8 @@ __global__ __launch_bounds__(64) void linear_up2_u8(
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
             const uint8_t *row = img + (size_t)jr[r] * row_bytes;
-            uint4 v[IN / 16];
-#pragma unroll
-            for (int k = 0; k < IN / 16; ++k) v[k] = ((const uint4 *)(row + (size_t)x0 * C))[k];
-            __builtin_memcpy(&px[r][C], v, IN);
+            // the chunk starts at x0 C = S C m bytes: 8-byte aligned
+            __builtin_memcpy(&px[r][C], __builtin_assume_aligned(row + (size_t)x0 * C, 8), IN);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 px[r][c] = row[(size_t)xl * C + c];
