@@ -40,8 +40,10 @@ _ABI_VERSION = 6
 _lib = None
 
 
-class ResizeError(RuntimeError):
-    """A non-zero status from the C ABI."""
+class ResizeError(ValueError, RuntimeError):
+    """A non-zero status from the C ABI, carrying resize_status_string's text.
+    A ValueError (most statuses reject arguments) and a RuntimeError (a
+    refused launch), so either kind of handler catches it."""
 
     def __init__(self, status: int, where: str):
         self.status = status
