@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--graph", type=int, default=0, metavar="B",
                    help="informational: also time the steps captured B at a time into a HIP "
                         "graph and replayed (small-image latency)")
+    p.add_argument("--no-trimmed", action="store_true",
+                   help="skip the per-launch event timing with trimming")
     p.add_argument("--no-copy", action="store_true",
                    help="skip the copy-kernel ceiling at the same bytes per launch")
     p.add_argument("--no-pipelined", action="store_true",
@@ -197,6 +199,25 @@ def cpu_baseline(w, src_np, mode, budget_s):
         "sample": "%d whole %s frame(s), %.1f s, %.2f ms per frame, output rows split "
                   "over %d host threads" % (reps, w.name, el, per * 1e3, threads),
     }
+
+
+def cpu_single_thread(w, src_np, mode, budget_s):
+    """The same oracle on one host thread, over whole frames, for about
+    budget_s seconds (at least one frame)."""
+    import oracle
+
+    fn = oracle.resize_linear if mode == "linear" else oracle.resize_nearest
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn(src_np, w.dH, w.dW)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / reps
+    return {"value": round(w.dst_pixels / per / 1e9, 4), "unit": "Gpix/s", "cores": 1,
+            "sample": "%d whole %s frame(s), %.1f s, %.2f ms per frame" % (reps, w.name, el, per * 1e3)}
 
 
 def main():
@@ -444,6 +465,29 @@ def main():
             "traffic": traffic,
         },
     }
+    # the measurement of "From Prototype to Performance" ("Measure
+    # performance carefully"): launches timed one by one with HIP events,
+    # sorted, 10 % trimmed at each end, averaged (informational)
+    if not args.no_trimmed:
+        R_ = 100
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(R_)]
+        torch.cuda.synchronize(dev)
+        bad = 0
+        for i, (ea, eb) in enumerate(evs):
+            j = i % pairs
+            ea.record(stream)
+            bad |= entry(sp[j], dp[j], N, H, W, C, code, dH, dW, sh)
+            eb.record(stream)
+        torch.cuda.synchronize(dev)
+        if bad:
+            raise R.ResizeError(bad, "resize")
+        d = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
+        cut = R_ // 10
+        kept = d[cut:R_ - cut]
+        line["trimmed_events"] = {"launches": R_, "trim": "10% each end",
+                                  "mean_us": round(sum(kept) / len(kept), 3),
+                                  "median_us": round(d[R_ // 2], 3)}
     # the copy-kernel ceiling at the same bytes per launch, and the HBM peak
     # the runtime reports (both informational)
     if not args.no_copy:
@@ -460,6 +504,7 @@ def main():
         line["graph_replay"] = graphed
     if not args.no_cpu and args.op == "resize":
         line["cpu_baseline"] = cpu_baseline(w, src_np, mode, args.cpu_seconds)
+        line["cpu_single_thread"] = cpu_single_thread(w, src_np, mode, min(3.0, args.cpu_seconds))
     print(json.dumps(line), flush=True)
 
 
