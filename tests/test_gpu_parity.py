@@ -560,3 +560,28 @@ def test_grey_4k_full_size():
     R.resize_linear_grey(src, dst)
     torch.cuda.synchronize()
     assert_parity(dst.cpu().numpy(), oracle.resize_linear_grey(s, w.dH, w.dW), "grey 4k")
+
+
+# --------------------------------------------------------------------------
+# batches beyond the 65535 grid extent: the exact 2x, exact 2:1, nearest and
+# direct kernels stride over images or rows past one grid's reach
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["up2", "half", "generic", "rowseg"])
+def test_batches_beyond_grid_extent(case, monkeypatch):
+    r = np.random.default_rng(1212)
+    N = 70000
+    if case == "up2":          # grid z = images, capped at 65535
+        shape, dst = (N, 1, 16, 1), (2, 32)
+    elif case == "half":       # grid y = output rows, capped at 65535
+        shape, dst = (N, 2, 32, 1), (1, 16)
+    elif case == "generic":    # direct kernels, many rows per band
+        monkeypatch.setenv("MI_RESIZE_PATH", "direct")
+        shape, dst = (N, 3, 5, 3), (2, 7)
+    else:                      # row-segment kernel, 2-row bands
+        monkeypatch.setenv("MI_RESIZE_PATH", "rowseg")
+        shape, dst = (N, 3, 5, 3), (2, 7)
+    s = random_image(r, shape, "u8")
+    for mode in ("linear", "nearest"):
+        say("case big batch %s %s %s -> %s" % (case, mode, shape, dst))
+        assert_parity(run_gpu(s, dst[0], dst[1], mode), run_oracle(s, dst[0], dst[1], mode),
+                      "big batch %s %s" % (case, mode))
