@@ -14,14 +14,25 @@ CASES = json.load(open(GOLDEN))["cases"]
 
 
 def arr(c):
-    return np.array(c["src"], dtype=np.uint8)[None, :, :, None]
+    a = np.array(c["src"], dtype=np.uint8)
+    return a[None, :, :, None] if a.ndim == 2 else a[None]
+
+
+def oracle_run(c):
+    dH, dW = c["dst_hw"]
+    m = c["mode"]
+    if m == "linear":
+        return oracle.resize_linear(arr(c), dH, dW)
+    if m == "grey":
+        return oracle.resize_linear_grey(arr(c), dH, dW)
+    if m.startswith("nearest_"):
+        return oracle.resize_nearest(arr(c), dH, dW, mapping=m[len("nearest_"):])
+    return oracle.resize_nearest(arr(c), dH, dW)
 
 
 @pytest.mark.parametrize("c", CASES, ids=[c["name"] for c in CASES])
 def test_oracle_reproduces(c):
-    dH, dW = c["dst_hw"]
-    f = oracle.resize_linear if c["mode"] == "linear" else oracle.resize_nearest
-    assert f(arr(c), dH, dW)[0, :, :, 0].tolist() == c["expected"]
+    assert oracle_run(c)[0, :, :, 0].tolist() == c["expected"]
 
 
 def by_name(n):
@@ -43,3 +54,18 @@ def test_closed_forms():
     assert by_name("ramp4_nearest_2x2")["expected"] == s[1::2, 1::2].tolist()
     assert by_name("ramp4_nearest_8x8")["expected"] == s.repeat(2, 0).repeat(2, 1).tolist()
     assert by_name("tie_2x2_to_1")["expected"] == [[1]]
+    # corner-aligned nearest: source index floor(4d/3) or floor(4d/3 + 1/2)
+    fl = [int(Fraction(4 * d, 3)) for d in range(3)]
+    ro = [min(int(Fraction(4 * d, 3) + Fraction(1, 2)), 3) for d in range(3)]
+    assert by_name("ramp4_nearest_floor_3x3")["expected"] == s[np.ix_(fl, fl)].tolist()
+    assert by_name("ramp4_nearest_round_3x3")["expected"] == s[np.ix_(ro, ro)].tolist()
+    # grey: the BT.601 weighted sum as an exact fraction, rounded half up
+    def grey(px):
+        r, g, b = (Fraction(v) for v in px[:3])
+        return int(Fraction(299, 1000) * r + Fraction(587, 1000) * g + Fraction(114, 1000) * b
+                   + Fraction(1, 2))
+    prim = by_name("grey_primaries")
+    assert prim["expected"] == [[grey(px) for px in prim["src"][0]]]
+    gt = by_name("grey_2x2_to_1")
+    greys = [grey(px) for row in gt["src"] for px in row]
+    assert gt["expected"] == [[(sum(greys) + 2) // 4]]

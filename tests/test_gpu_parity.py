@@ -187,9 +187,22 @@ def test_golden_hand_cases():
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
     for c in json.load(open(path))["cases"]:
         say("case golden %s" % c["name"])
-        s = np.array(c["src"], dtype=np.uint8)[None, :, :, None]
+        a = np.array(c["src"], dtype=np.uint8)
+        s = a[None, :, :, None] if a.ndim == 2 else a[None]
         dH, dW = c["dst_hw"]
-        got = run_gpu(s, dH, dW, c["mode"])[0, :, :, 0]
+        m = c["mode"]
+        if m in ("linear", "nearest"):
+            got = run_gpu(s, dH, dW, m)[0, :, :, 0]
+        else:
+            src = torch.from_numpy(s).cuda()
+            C = 1 if m == "grey" else s.shape[3]
+            dst = torch.empty((1, dH, dW, C), dtype=torch.uint8, device="cuda")
+            if m == "grey":
+                R.resize_linear_grey(src, dst)
+            else:
+                R.resize_nearest_mapping(src, dst, mapping=m[len("nearest_"):])
+            torch.cuda.synchronize()
+            got = dst.cpu().numpy()[0, :, :, 0]
         assert got.tolist() == c["expected"], c["name"]
 
 
