@@ -223,8 +223,8 @@ def cpu_single_thread(w, src_np, mode, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the resize runs on one GPU and has no "
+              "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args)
