@@ -147,6 +147,11 @@ constexpr int kSegLdsBudget = 16 * 1024;
 // more than they gain.
 constexpr long long kSegTargetBands = 65536;
 constexpr long long kSegMinBandRows = 2;
+// Where each output pixel is a single byte (grey output, one-channel uint8),
+// a row moves little and the per-band set-up weighs more: three-row bands
+// (thumbnail batch to grey 48.6 -> 44.4 us, 2x one-channel enlargement on
+// this kernel 15.5 -> 13.5 us; wider outputs measured better or equal at two).
+constexpr long long kSegMinBandRowsNarrow = 3;
 // A crop-then-resize band first reads its image's region from device memory
 // before it can map a row, so its bands are made longer to amortise that
 // round trip (random crops of the thumbnail batch: 2 rows 44.9 us, 4 rows
@@ -205,8 +210,11 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const long long rows = (long long)batch * dH;
     SegPlan pl;
     // a crop is at most W wide, so the whole-image bound covers every crop
-    if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows,
-                     ROI ? kSegMinBandRowsRoi : kSegMinBandRows, pl))
+    constexpr int out_px_bytes =
+        OUT == kOutGrey ? (int)sizeof(T) : (OUT == kOutSame ? C * (int)sizeof(T) : 4 * C);
+    const long long min_rows = ROI ? kSegMinBandRowsRoi
+                                   : (out_px_bytes == 1 ? kSegMinBandRowsNarrow : kSegMinBandRows);
+    if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, min_rows, pl))
         return false;
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8;
     // a slot then holds 64 lanes x that many chunks (the kernel writes its
