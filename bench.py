@@ -162,6 +162,18 @@ def copy_same_bytes(total_bytes, steps, lib, dev, sh):
     return {"bytes_moved": 2 * n, "kernel_us": round(us, 3), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}
 
 
+def host_cpu_model():
+    """The host CPU's model name as /proc/cpuinfo gives it ("unknown" elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, src_np, mode, budget_s):
     """The CPU oracle as it stands, on the host cores, over whole frames of
     the same workload, repeated until about budget_s seconds have passed."""
@@ -197,7 +209,8 @@ def cpu_baseline(w, src_np, mode, budget_s):
         "cores": threads,
         "kind": "oracle",
         "sample": "%d whole %s frame(s), %.1f s, %.2f ms per frame, output rows split "
-                  "over %d host threads" % (reps, w.name, el, per * 1e3, threads),
+                  "over %d host threads of %d (%s)" % (reps, w.name, el, per * 1e3, threads,
+                                                       os.cpu_count() or 1, host_cpu_model()),
     }
 
 

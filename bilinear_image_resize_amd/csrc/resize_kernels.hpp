@@ -462,152 +462,196 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     }
 }
 
+// Orders this wave's LDS accesses before and after it.  A wave's LDS
+// operations complete in issue order, so keeping the compiler from moving
+// them across this point is all the synchronisation a wave-private slot needs.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Writes one wave's output row segment back to device memory.  The segment
+// sits in LDS lane-major (lane L's OUT bytes at L * OUT); store k of every
+// lane takes bytes [1024 k + 16 L, +16), so each store instruction of the
+// wave covers 1 KiB of whole cache lines, which the non-temporal hint needs
+// to pay (strided 16-byte pieces of a lane's own chunk would leave partial
+// lines).  seg_bytes = active lanes * OUT.
+template <int OUT>
+__device__ __forceinline__ void store_staged(const uint8_t *lds, uint8_t *out, int seg_bytes,
+                                             int lane)
+{
+    static_assert(OUT % 16 == 0, "whole 16-byte pieces");
+#pragma unroll
+    for (int k = 0; k < OUT / 16; ++k) {
+        const int b = 1024 * k + 16 * lane;
+        if (b < seg_bytes)
+            __builtin_nontemporal_store(*(const u32x4_t *)(lds + b), (u32x4_t *)(out + b));
+    }
+}
+
 // --------------------------------------------------------------------------
-// Exact 2x upscale of uint8 (dH = 2 H, dW = 2 W).  Output column 2k + 1 sits
-// at source coordinate k + 1/4 and column 2k + 2 at k + 3/4, so the 11-bit
+// Exact 2x upscale of uint8 (dH = 2 H, dW = 2 W).  Output column 2k sits at
+// source coordinate k - 1/4 and column 2k + 1 at k + 1/4, so the 11-bit
 // weights are exactly 512 and 1536 and the general formula reduces, bit for
-// bit, to (sum of k_ij p_ij + 8) >> 4 with k_ij in {9, 3, 3, 1}.  Edge taps
-// clamp to the first / last pixel, which the kernel reproduces by
-// replicating them (a clamped tap pair is one pixel with weight 16).
+// bit, to (sum of k_ij p_ij + 8) >> 4 with k_ij in {9, 3, 3, 1}: a
+// horizontal 1:3 or 3:1 sum h per source row, then (3 h_a + h_b + 8) >> 4
+// down the column.  Edge taps clamp to the first / last pixel.
 //
-// A lane owns S consecutive source pixels of one source row j and writes
-// output rows 2j and 2j + 1, columns [2 S m, 2 S m + 2 S): it reads source
-// rows j - 1, j, j + 1 (clamped) over pixels -1 .. S (the outer two clamped),
-// forms the horizontal 1:3 / 3:1 sums per row, then the vertical ones.
-// Needs W % S == 0, W * C % 16 == 0 and 16-byte aligned buffers.
-// Grid: x = 64-lane workgroups across a row, y = source row j of an image,
-// z = image (stride gridDim.z), so no lane divides to find its image.
+// Rows: a wave takes the gap g (-1 .. H - 1) between source rows g and
+// g + 1 (clamped) and writes output rows 2g + 1 (3:1) and 2g + 2 (1:3), of
+// which the first gap has only the second and the last only the first, so
+// each source row is read by two waves, not three.
+//
+// Columns: a lane owns S source pixels (chunk m, IN = S C bytes) and writes
+// the OUT = 2 IN output bytes [OUT m, OUT m + OUT) of both rows.  It loads
+// the chunk as dwords with one dword of neighbours on each side (a copy of
+// its own edge pixel where the row ends), so every tap is a constant byte
+// position in that window.  Output bytes go in pairs (k, k + 1), one per
+// 16-bit half: each output byte is 1 x one tap + 3 x another, so a pair is
+// one v_pk_mad_u16 of two byte pairs picked with v_perm_b32 (any two bytes
+// at most 4 apart lie in two consecutive dwords).  All sums stay below
+// 2^16: h <= 1020 and 48 h_a + 16 h_b + 128 <= 65408, whose high byte is
+// (3 h_a + h_b + 8) >> 4, so the rounding shift is a byte selection.
+//
+// Needs W % S == 0, W C % 16 == 0 and 16-byte aligned buffers.  Workgroup:
+// RB waves, one gap each.  Grid: x = 64-chunk segments across a row, y =
+// groups of RB gaps of an image, z = image (stride gridDim.z).  Stores are
+// non-temporal (the output is not read back); chunks wider than 16 bytes
+// per output row go out through LDS so that every store instruction covers
+// whole cache lines.
 // --------------------------------------------------------------------------
 template <int C> struct Up2Shape { static constexpr int S = C == 4 ? 8 : 16; };
-// source pixels per lane of the linear kernel: its own (smaller) chunks put
-// more waves on a frame than the nearest kernel needs
+// source pixels per lane of the linear kernel
 template <int C> struct Up2LinShape { static constexpr int S = C == 4 ? 4 : 8; };
 
-template <int C>
-__global__ __launch_bounds__(64) void linear_up2_u8(
+// Byte position, in a lane's dword window, of the tap that output byte k of
+// its chunk weights by 1 (W1) or by 3 (!W1).  Output byte k is channel k % C
+// of output pixel q = k / C, which takes source pixel q / 2 with weight 3
+// and its left (q even) or right (q odd) neighbour with weight 1; source
+// pixel i (-1 .. S) channel c sits at 4 + i C + c.
+template <int C, bool W1>
+__host__ __device__ constexpr int up2_tap(int k)
+{
+    const int q = k / C, c = k % C, i = q / 2;
+    return 4 + (W1 ? (q % 2 ? i + 1 : i - 1) : i) * C + c;
+}
+
+// Selector of __builtin_amdgcn_perm(e[d + 1], e[d], sel) that zero-extends
+// window bytes a and b (both in dwords d, d + 1) into the low and high
+// 16-bit halves.
+__host__ __device__ constexpr uint32_t up2_pair_sel(int a, int b, int d)
+{
+    return 0x0c000c00u | (uint32_t)(a - 4 * d) | ((uint32_t)(b - 4 * d) << 16);
+}
+
+// Output byte pair (k, k + 1) of one row's taps of weight 1 (W1) or 3 from
+// the ND-dword window e.  The two dwords start at the lower tap's dword,
+// moved back one when that is the window's last.
+template <int C, bool W1, int ND>
+__device__ __forceinline__ uint32_t up2_pick(const uint32_t (&e)[ND], int k)
+{
+    // k is a compile-time constant after unrolling, so are d and the selector
+    const int a = up2_tap<C, W1>(k), b = up2_tap<C, W1>(k + 1);
+    const int lo = (a < b ? a : b) / 4;
+    const int d = lo < ND - 2 ? lo : ND - 2;
+    return __builtin_amdgcn_perm(e[d + 1], e[d], up2_pair_sel(a, b, d));
+}
+
+template <int C, int RB>
+__global__ __launch_bounds__(64 * RB) void linear_up2_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
     int batch, int chunks_per_row)
 {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     constexpr int S = Up2LinShape<C>::S;
-    constexpr int IN = S * C;              // bytes of one source row chunk (multiple of 8)
-    constexpr int OUT = 2 * S * C;         // bytes of one output row chunk (multiple of 16)
-    static_assert(IN % 8 == 0 && OUT % 16 == 0, "chunk shape");
-    const int m = blockIdx.x * 64 + threadIdx.x;
-    if (m >= chunks_per_row) return;
+    constexpr int IN = S * C;              // source bytes of a chunk
+    constexpr int OUT = 2 * IN;            // output bytes of a chunk per row
+    constexpr int NP = OUT / 2;            // output byte pairs per row
+    constexpr int ND = IN / 4 + 2;         // window dwords
+    static_assert(IN % 4 == 0 && OUT % 16 == 0 && C <= 4, "chunk shape");
+    static_assert(up2_tap<C, true>(0) >= 4 - C && up2_tap<C, true>(OUT - 1) < 4 * ND,
+                  "taps inside the window");
+    constexpr bool STAGE = OUT > 16;       // wider chunks go out through LDS
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? RB * 2 * 64 * OUT : 16];
+    const int lane = threadIdx.x;
+    const int m = blockIdx.x * 64 + lane;
+    const int g = (int)(blockIdx.y * RB + threadIdx.y) - 1;   // gap, uniform across the wave
+    const bool active = m < chunks_per_row;
+    if (g >= H || (!STAGE && !active)) return;
     const size_t row_bytes = (size_t)W * C;
-    const int x0 = m * S;                                  // first source pixel of the chunk
-    const int xl = x0 > 0 ? x0 - 1 : 0;                    // left neighbour (clamped)
-    const int xr = x0 + S < W ? x0 + S : W - 1;            // right neighbour (clamped)
-    const int j = blockIdx.y;
-    if constexpr (C == 1) {
-        // Packed form: pairs of neighbouring bytes sit in the two 16-bit
-        // halves of a register (all sums stay below 4096, exact in 16 bits).
-        // For source pair k (bytes 2k, 2k + 1 of the chunk) and one source
-        // row: A = the left neighbours, B = the pair itself, R = the right
-        // neighbours; even outputs A + 3B, odd outputs 3B + R.
-        static_assert(S == 8, "the packed form below is written for 8-byte chunks");
-        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-        auto pair = [](uint32_t hi, uint32_t lo, uint32_t sel) {
-            return __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(hi, lo, sel));
-        };
-        const int jr[3] = {j > 0 ? j - 1 : 0, j, j + 1 < H ? j + 1 : H - 1};
-        for (int n = blockIdx.z; n < batch; n += gridDim.z) {
-            const uint8_t *img = src + (size_t)n * H * row_bytes;
-            u16x2 hE[3][S / 2], hO[3][S / 2];
+    const int ra = g > 0 ? g : 0, rb = g + 1 < H ? g + 1 : H - 1;
+    const bool has_a = g >= 0, has_b = g + 1 < H;    // output rows 2g + 1, 2g + 2
+    const bool left = m > 0, right = (m + 1) * S < W;
+    // horizontal sums of one source row, one u16x2 per output byte pair
+    auto hsum = [&](const uint8_t *row, u16x2 (&h)[NP]) {
+        const uint8_t *p = row + (size_t)m * IN;      // 4-byte aligned
+        uint32_t e[ND];
+        __builtin_memcpy(&e[1], __builtin_assume_aligned(p, IN % 16 == 0 ? 16 : 8), IN);
+        // neighbours: the adjacent dword, or at a row end the chunk's own
+        // edge dword with its edge pixel moved into place.  Both loads are
+        // unconditional (clamped addresses) so that all of them issue before
+        // the first wait.
+        const uint32_t lw = *(const uint32_t *)(p + (left ? -4 : 0));
+        const uint32_t rw = *(const uint32_t *)(p + (right ? IN : IN - 4));
+        e[0] = left ? lw : lw << (8 * (4 - C));
+        e[ND - 1] = right ? rw : rw >> (8 * (4 - C));
 #pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                const uint8_t *row = img + (size_t)jr[r] * row_bytes;
-                uint2 w;
-                __builtin_memcpy(&w, __builtin_assume_aligned(row + x0, 8), 8);
-                const uint32_t lw = row[xl], rw = row[xr];
-                // bytes 0-3 of {hi:lo} are lo's, 4-7 hi's; 0x0c gives a zero byte
-                u16x2 Bv[4], Rv[4];
-                Bv[0] = pair(w.y, w.x, 0x0c010c00u);
-                Bv[1] = pair(w.y, w.x, 0x0c030c02u);
-                Bv[2] = pair(w.y, w.x, 0x0c050c04u);
-                Bv[3] = pair(w.y, w.x, 0x0c070c06u);
-                Rv[0] = pair(w.y, w.x, 0x0c020c01u);
-                Rv[1] = pair(w.y, w.x, 0x0c040c03u);
-                Rv[2] = pair(w.y, w.x, 0x0c060c05u);
-                Rv[3] = pair(rw, w.y, 0x0c040c03u);
-                const u16x2 A0 = pair(w.x, lw, 0x0c040c00u);
-#pragma unroll
-                for (int k = 0; k < S / 2; ++k) {
-                    const u16x2 Av = k == 0 ? A0 : Rv[k - 1];
-                    const u16x2 b3 = Bv[k] * (unsigned short)3;
-                    hE[r][k] = Av + b3;
-                    hO[r][k] = b3 + Rv[k];
-                }
-            }
-            uint32_t o0[S / 2], o1[S / 2];
-#pragma unroll
-            for (int k = 0; k < S / 2; ++k) {
-                const u16x2 tE = hE[1][k] * (unsigned short)3 + (unsigned short)8;
-                const u16x2 tO = hO[1][k] * (unsigned short)3 + (unsigned short)8;
-                const u16x2 e0 = (tE + hE[0][k]) >> (unsigned short)4, e1 = (tE + hE[2][k]) >> (unsigned short)4;
-                const u16x2 d0 = (tO + hO[0][k]) >> (unsigned short)4, d1 = (tO + hO[2][k]) >> (unsigned short)4;
-                // output bytes E[2k], O[2k], E[2k+1], O[2k+1]
-                o0[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d0),
-                                              __builtin_bit_cast(uint32_t, e0), 0x06020400u);
-                o1[k] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d1),
-                                              __builtin_bit_cast(uint32_t, e1), 0x06020400u);
-            }
-            uint8_t *d0p = dst + ((size_t)n * 2 * H + 2 * j) * (2 * row_bytes) + (size_t)x0 * 2;
-            uint8_t *d1p = d0p + 2 * row_bytes;
-#pragma unroll
-            for (int k = 0; k < OUT / 16; ++k) {
-                ((uint4 *)d0p)[k] = make_uint4(o0[4 * k], o0[4 * k + 1], o0[4 * k + 2], o0[4 * k + 3]);
-                ((uint4 *)d1p)[k] = make_uint4(o1[4 * k], o1[4 * k + 1], o1[4 * k + 2], o1[4 * k + 3]);
-            }
+        for (int j = 0; j < NP; ++j) {
+            const u16x2 u = __builtin_bit_cast(u16x2, up2_pick<C, true, ND>(e, 2 * j));
+            const u16x2 v = __builtin_bit_cast(u16x2, up2_pick<C, false, ND>(e, 2 * j));
+            h[j] = v * (unsigned short)3 + u;
         }
-        return;
-    }
+    };
+    // high bytes of 48 h_x + 16 h_y + 128 for four output bytes
+    auto vsum = [](const u16x2 (&hx)[NP], const u16x2 (&hy)[NP], int w) {
+        const u16x2 z0 = hx[2 * w] * (unsigned short)48 +
+                         (hy[2 * w] * (unsigned short)16 + (unsigned short)128);
+        const u16x2 z1 = hx[2 * w + 1] * (unsigned short)48 +
+                         (hy[2 * w + 1] * (unsigned short)16 + (unsigned short)128);
+        return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, z1),
+                                     __builtin_bit_cast(uint32_t, z0), 0x07050301u);
+    };
+    uint8_t *lds0 = lds_all + threadIdx.y * 2 * 64 * OUT, *lds1 = lds0 + 64 * OUT;
+    const int seg_bytes = min(64, chunks_per_row - (int)blockIdx.x * 64) * OUT;
     for (int n = blockIdx.z; n < batch; n += gridDim.z) {
         const uint8_t *img = src + (size_t)n * H * row_bytes;
-        const int jr[3] = {j > 0 ? j - 1 : 0, j, j + 1 < H ? j + 1 : H - 1};
-        // px[r][i]: row r, pixel i - 1 (i = 0 .. S + 1), channel-interleaved bytes
-        uint8_t px[3][(S + 2) * C];
+        // output row 2g + 2 of image n; row 2g + 1 precedes it (and exists
+        // only when has_a, so da is formed only then)
+        const size_t off_b = ((size_t)n * 2 * H + (size_t)(2 * g + 2)) * (2 * row_bytes) +
+                          (size_t)blockIdx.x * 64 * OUT;
+        if (active) {
+            u16x2 ha[NP], hb[NP];
+            hsum(img + (size_t)ra * row_bytes, ha);
+            hsum(img + (size_t)rb * row_bytes, hb);
+            uint32_t oa[OUT / 4], ob[OUT / 4];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            const uint8_t *row = img + (size_t)jr[r] * row_bytes;
-            // the chunk starts at x0 C = S C m bytes: 8-byte aligned
-            __builtin_memcpy(&px[r][C], __builtin_assume_aligned(row + (size_t)x0 * C, 8), IN);
+            for (int w = 0; w < OUT / 4; ++w) {
+                oa[w] = vsum(ha, hb, w);      // row 2g + 1: 3 x row g + row g + 1
+                ob[w] = vsum(hb, ha, w);      // row 2g + 2: row g + 3 x row g + 1
+            }
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                px[r][c] = row[(size_t)xl * C + c];
-                px[r][(S + 1) * C + c] = row[(size_t)xr * C + c];
+            for (int k = 0; k < OUT / 16; ++k) {
+                const u32x4_t qa = {oa[4 * k], oa[4 * k + 1], oa[4 * k + 2], oa[4 * k + 3]};
+                const u32x4_t qb = {ob[4 * k], ob[4 * k + 1], ob[4 * k + 2], ob[4 * k + 3]};
+                if constexpr (STAGE) {
+                    *(u32x4_t *)(lds0 + lane * OUT + 16 * k) = qa;
+                    *(u32x4_t *)(lds1 + lane * OUT + 16 * k) = qb;
+                } else {
+                    // one 16-byte piece per lane and row: already lane-contiguous
+                    if (has_a)
+                        __builtin_nontemporal_store(
+                            qa, (u32x4_t *)(dst + (off_b - 2 * row_bytes) + lane * OUT));
+                    if (has_b) __builtin_nontemporal_store(qb, (u32x4_t *)(dst + off_b + lane * OUT));
+                }
             }
         }
-        // horizontal sums, 4x scale: even output column 2i takes pixels
-        // (i - 1, i) with weights (1, 3); odd column 2i + 1 takes (i, i + 1)
-        // with (3, 1)
-        unsigned short hs[3][2 * S * C];
-#pragma unroll
-        for (int r = 0; r < 3; ++r)
-#pragma unroll
-            for (int i = 0; i < S; ++i)
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const unsigned a = px[r][i * C + c], b = px[r][(i + 1) * C + c],
-                                   d = px[r][(i + 2) * C + c];
-                    hs[r][(2 * i) * C + c] = (unsigned short)(a + 3 * b);
-                    hs[r][(2 * i + 1) * C + c] = (unsigned short)(3 * b + d);
-                }
-        uint8_t o0[OUT], o1[OUT];
-#pragma unroll
-        for (int k = 0; k < 2 * S * C; ++k) {
-            o0[k] = (uint8_t)((hs[0][k] + 3u * hs[1][k] + 8u) >> 4);   // row 2j: rows (j-1, j)
-            o1[k] = (uint8_t)((3u * hs[1][k] + hs[2][k] + 8u) >> 4);   // row 2j+1: rows (j, j+1)
-        }
-        uint8_t *d0 = dst + ((size_t)n * 2 * H + 2 * j) * (2 * row_bytes) + (size_t)x0 * 2 * C;
-        uint8_t *d1 = d0 + 2 * row_bytes;
-#pragma unroll
-        for (int k = 0; k < OUT / 16; ++k) {
-            uint4 a, b;
-            __builtin_memcpy(&a, o0 + 16 * k, 16);
-            __builtin_memcpy(&b, o1 + 16 * k, 16);
-            ((uint4 *)d0)[k] = a;
-            ((uint4 *)d1)[k] = b;
+        if constexpr (STAGE) {
+            wave_sync();
+            if (has_a) store_staged<OUT>(lds0, dst + (off_b - 2 * row_bytes), seg_bytes, lane);
+            if (has_b) store_staged<OUT>(lds1, dst + off_b, seg_bytes, lane);
+            wave_sync();
         }
     }
 }
@@ -617,42 +661,62 @@ __global__ __launch_bounds__(64) void linear_up2_u8(
 // coordinate of output column d is floor((2d + 1) / 4) = d / 2, so the
 // output is every source pixel repeated twice in both directions.  A lane
 // reads S pixels of source row j and writes them doubled to output rows 2j
-// and 2j + 1.  Same shape rules and grid as linear_up2_u8.
+// and 2j + 1.  Same shape rules, workgroup and stores as linear_up2_u8; the
+// grid's y runs over groups of RB rows of all N H source rows (strided
+// past the grid's extent).
 // --------------------------------------------------------------------------
-template <int C>
-__global__ __launch_bounds__(64) void nearest_up2_u8(
-    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int /* H: unused, the
-    argument list matches linear_up2_u8 */, int W, long long rows, int chunks_per_row)
+template <int C, int RB>
+__global__ __launch_bounds__(64 * RB) void nearest_up2_u8(
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int W, long long rows,
+    int chunks_per_row)
 {
     constexpr int S = Up2Shape<C>::S;
     constexpr int IN = S * C;
     constexpr int OUT = 2 * S * C;
-    const int m = blockIdx.x * 64 + threadIdx.x;
-    if (m >= chunks_per_row) return;
+    constexpr bool STAGE = OUT > 16;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? RB * 64 * OUT : 16];
+    const int lane = threadIdx.x;
+    const int m = blockIdx.x * 64 + lane;
+    const bool active = m < chunks_per_row;
+    if (!STAGE && !active) return;
     const size_t row_bytes = (size_t)W * C;
-    for (long long t = blockIdx.y; t < rows; t += gridDim.y) {
-        uint4 v[IN / 16];
-        const uint8_t *row = src + (size_t)t * row_bytes + (size_t)m * IN;
-#pragma unroll
-        for (int k = 0; k < IN / 16; ++k) v[k] = ((const uint4 *)row)[k];
-        uint8_t in[IN], out[OUT];
-        __builtin_memcpy(in, v, IN);
-#pragma unroll
-        for (int i = 0; i < S; ++i)
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                out[(2 * i) * C + c] = in[i * C + c];
-                out[(2 * i + 1) * C + c] = in[i * C + c];
-            }
+    uint8_t *lds = lds_all + threadIdx.y * 64 * OUT;
+    const int seg_bytes = min(64, chunks_per_row - (int)blockIdx.x * 64) * OUT;
+    // t is uniform across the wave
+    for (long long t = (long long)blockIdx.y * RB + threadIdx.y; t < rows;
+         t += (long long)gridDim.y * RB) {
         // source row t of the flattened N*H rows feeds output rows 2t, 2t + 1
-        uint8_t *d0 = dst + (size_t)(2 * t) * (2 * row_bytes) + (size_t)m * OUT;
-        uint8_t *d1 = d0 + 2 * row_bytes;
+        uint8_t *d0 = dst + (size_t)(2 * t) * (2 * row_bytes) + (size_t)blockIdx.x * 64 * OUT;
+        if (active) {
+            // the chunk starts at m * IN bytes into a row of W C bytes (a
+            // multiple of 16): aligned to 16 bytes, or to IN when IN < 16
+            const uint8_t *row = src + (size_t)t * row_bytes + (size_t)m * IN;
+            uint8_t in[IN], out[OUT];
+            __builtin_memcpy(in, __builtin_assume_aligned(row, IN < 16 ? IN : 16), IN);
 #pragma unroll
-        for (int k = 0; k < OUT / 16; ++k) {
-            uint4 q;
-            __builtin_memcpy(&q, out + 16 * k, 16);
-            ((uint4 *)d0)[k] = q;
-            ((uint4 *)d1)[k] = q;
+            for (int i = 0; i < S; ++i)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    out[(2 * i) * C + c] = in[i * C + c];
+                    out[(2 * i + 1) * C + c] = in[i * C + c];
+                }
+#pragma unroll
+            for (int k = 0; k < OUT / 16; ++k) {
+                u32x4_t q;
+                __builtin_memcpy(&q, out + 16 * k, 16);
+                if constexpr (STAGE) {
+                    *(u32x4_t *)(lds + lane * OUT + 16 * k) = q;
+                } else {
+                    __builtin_nontemporal_store(q, (u32x4_t *)(d0 + lane * OUT));
+                    __builtin_nontemporal_store(q, (u32x4_t *)(d0 + 2 * row_bytes + lane * OUT));
+                }
+            }
+        }
+        if constexpr (STAGE) {
+            wave_sync();
+            store_staged<OUT>(lds, d0, seg_bytes, lane);
+            store_staged<OUT>(lds, d0 + 2 * row_bytes, seg_bytes, lane);
+            wave_sync();
         }
     }
 }
@@ -744,16 +808,6 @@ constexpr int kSegReadSlack = 16;  // bytes a two-tap LDS read may run past the 
 constexpr int kSegWaves = 4;
 
 __device__ __forceinline__ int seg_lane() { return (int)threadIdx.x & (kSegLanes - 1); }
-
-// Orders this wave's LDS accesses before and after it.  A wave's LDS
-// operations complete in issue order, so keeping the compiler from moving
-// them across this point is all the synchronisation a wave-private slot needs.
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // One source-row segment to stage: `bytes` bytes from p (uniform across the
 // wave) into an LDS slot, as 16-byte chunks from the 16-byte boundary at or

@@ -154,6 +154,23 @@ def test_double_upscale_shapes(C):
                           "up2 %s %s" % (mode, (C, N, H, W)))
 
 
+@pytest.mark.parametrize("C", [1, 3, 4])
+def test_double_upscale_random_shapes(C):
+    """Seeded random shapes that the exact 2x kernels take (widths a multiple
+    of 16): row counts around the waves per workgroup, several 64-chunk
+    segments per row with a partial last one, and batches."""
+    r = np.random.default_rng(4040 + C)
+    for i in range(40):
+        N = int(r.integers(1, 4))
+        H = int(r.integers(1, 70))
+        W = 16 * int(r.integers(1, 21))
+        s = random_image(r, (N, H, W, C), "u8")
+        for mode in ("linear", "nearest"):
+            say("case up2 random %d %s C=%d N=%d src=%dx%d" % (i, mode, C, N, H, W))
+            assert_parity(run_gpu(s, 2 * H, 2 * W, mode), run_oracle(s, 2 * H, 2 * W, mode),
+                          "up2 random %s %s" % (mode, (C, N, H, W)))
+
+
 # --------------------------------------------------------------------------
 # degenerate and extreme shapes
 # --------------------------------------------------------------------------
@@ -583,8 +600,8 @@ def test_grey_4k_full_size():
 def test_batches_beyond_grid_extent(case, monkeypatch):
     r = np.random.default_rng(1212)
     N = 70000
-    if case == "up2":          # grid z = images, capped at 65535
-        shape, dst = (N, 1, 16, 1), (2, 32)
+    if case == "up2":          # grid z = images (linear) or y = rows / 2 (nearest), capped at 65535
+        shape, dst = (2 * N, 1, 16, 1), (2, 32)
     elif case == "half":       # grid y = output rows, capped at 65535
         shape, dst = (N, 2, 32, 1), (1, 16)
     elif case == "generic":    # direct kernels, many rows per band
