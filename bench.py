@@ -34,12 +34,12 @@ INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
 # dispatch), each scaled by the factor the same counter reads for the plain
 # 16-byte copy of 32 MiB (`bench.py --copy-calibration 33554432`: FETCH_SIZE
-# 16390.74 KiB -> x 1.9992, WRITE_SIZE 32804.77 KiB -> x 0.9989).  Valid only
+# 16390.74 KiB -> x 1.9992, WRITE_SIZE 32798.97 KiB -> x 0.9991).  Valid only
 # for the kernel named; profiles/linear_half_u8_4k_rgb_pmc_traffic.md holds
 # the runs.  Workloads without an entry report null.
 MEASURED_TRAFFIC = {
     ("4k", "linear"): {"kernel": "linear_half_u8<3, false>", "fetch_kib": 12169.14, "write_kib": 6075.0,
-                       "fetch_scale": 1.9992, "write_scale": 0.9989},
+                       "fetch_scale": 1.9992, "write_scale": 0.9991},
 }
 
 
