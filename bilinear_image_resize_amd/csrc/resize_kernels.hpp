@@ -434,7 +434,10 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     const int n16 = seg_px * 2 * C / 16;          // whole: dW meets the divisibility rule
     const size_t src_row = (size_t)2 * dW * C;
     const size_t dst_row = (size_t)dW * OC;
-    for (long long g = blockIdx.y; g < rows; g += gridDim.y) {
+    // the grid's y extent never exceeds rows, so every workgroup has a
+    // first row: a do-while lets all arguments load at once
+    long long g = blockIdx.y;
+    do {
         const uint8_t *s0 = src + (size_t)(2 * g) * src_row + (size_t)seg * SRC_B;
         const uint8_t *s1 = s0 + src_row;
         uint4 va[NL], vb[NL];
@@ -497,7 +500,8 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
             }
         }
         wave_sync();
-    }
+        g += gridDim.y;
+    } while (g < rows);
 }
 
 // --------------------------------------------------------------------------
