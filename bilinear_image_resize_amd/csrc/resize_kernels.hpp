@@ -474,11 +474,42 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
                     r[k] = (uint8_t)((s4 + 2u) >> 2);
                 }
             } else {
+                // output byte k = (a[p] + a[p + C] + b[p] + b[p + C] + 2) >> 2
+                // with p = 2k - k % C, computed for pairs of output bytes,
+                // one per 16-bit half: the four taps are picked as byte pairs
+                // with v_perm_b32 (two bytes at most 4 apart lie in two
+                // consecutive dwords) and added with v_pk_add_u16; the sum s
+                // <= 1020 gives 64 s + 128 <= 65408, whose high byte is
+                // (s + 2) >> 2.  About 40% fewer VALU ops than byte by byte
+                // (4K -> 1080p RGB 6.61-6.80 -> 6.54-6.70 us, grey 3.81 ->
+                // 3.59 us).
+                typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+                uint32_t aw[LB / 4], bw[LB / 4], ow[OB / 4];
+                __builtin_memcpy(aw, a, LB);
+                __builtin_memcpy(bw, b, LB);
+                auto pick = [](const uint32_t (&w)[LB / 4], int i, int j) {
+                    const int lo = (i < j ? i : j) / 4;
+                    const int d = lo < LB / 4 - 2 ? lo : LB / 4 - 2;
+                    return __builtin_bit_cast(
+                        u16x2, __builtin_amdgcn_perm(w[d + 1], w[d],
+                                                     0x0c000c00u | (uint32_t)(i - 4 * d) |
+                                                         ((uint32_t)(j - 4 * d) << 16)));
+                };
+                u16x2 z[OB / 2];
 #pragma unroll
-                for (int k = 0; k < OB; ++k) {
-                    const int p = 2 * k - k % C;  // first source byte of output byte k
-                    r[k] = (uint8_t)(((unsigned)a[p] + a[p + C] + b[p] + b[p + C] + 2u) >> 2);
+                for (int h = 0; h < OB / 2; ++h) {
+                    const int k = 2 * h;
+                    const int p0 = 2 * k - k % C, p1 = 2 * (k + 1) - (k + 1) % C;
+                    const u16x2 sum = pick(aw, p0, p1) + pick(aw, p0 + C, p1 + C) +
+                                      pick(bw, p0, p1) + pick(bw, p0 + C, p1 + C);
+                    z[h] = sum * (unsigned short)64 + (unsigned short)128;
                 }
+#pragma unroll
+                for (int w = 0; w < OB / 4; ++w)
+                    ow[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, z[2 * w + 1]),
+                                                  __builtin_bit_cast(uint32_t, z[2 * w]),
+                                                  0x07050301u);
+                __builtin_memcpy(r, ow, OB);
             }
         }
         uint8_t *o = dst + (size_t)g * dst_row + (size_t)seg * SEG * OC + (size_t)lane * OB;
