@@ -138,6 +138,30 @@ def test_half_downscale_shapes(C):
         assert_parity(run_gpu(s, dH, dW), run_oracle(s, dH, dW), "half %s" % ((C, N, dH, dW),))
 
 
+@pytest.mark.parametrize("C", [1, 3, 4])
+def test_half_downscale_random_shapes(C):
+    """Seeded random shapes that the exact 2:1 kernel takes (output widths a
+    multiple of 16, 8 or 4 for 1, 3 or 4 channels): several 256- or
+    1024-pixel segments per row with a partial last one, odd row counts and
+    batches; for 3 and 4 channels also the grey output."""
+    q = {1: 16, 3: 8, 4: 4}[C]
+    r = np.random.default_rng(5050 + C)
+    for i in range(40):
+        N = int(r.integers(1, 4))
+        dH = int(r.integers(1, 40))
+        dW = q * int(r.integers(1, 2200 // q))
+        s = random_image(r, (N, 2 * dH, 2 * dW, C), "u8")
+        say("case half random %d C=%d N=%d dst=%dx%d" % (i, C, N, dH, dW))
+        assert_parity(run_gpu(s, dH, dW), run_oracle(s, dH, dW), "half random %s" % ((C, N, dH, dW),))
+        if C >= 3:
+            src = torch.from_numpy(s).cuda()
+            dst = torch.empty((N, dH, dW, 1), dtype=src.dtype, device="cuda")
+            R.resize_linear_grey(src, dst)
+            torch.cuda.synchronize()
+            assert_parity(dst.cpu().numpy(), oracle.resize_linear_grey(s, dH, dW),
+                          "half grey random %s" % ((C, N, dH, dW),))
+
+
 # --------------------------------------------------------------------------
 # exact 2x upscale (its own kernel): channel counts, batches, one-row and
 # one-chunk images, and widths that fall back to the generic kernels
