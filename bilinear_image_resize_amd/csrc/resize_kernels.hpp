@@ -661,8 +661,8 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
     const int seg_bytes = min(64, chunks_per_row - (int)blockIdx.x * 64) * OUT;
     for (int n = blockIdx.z; n < batch; n += gridDim.z) {
         const uint8_t *img = src + (size_t)n * H * row_bytes;
-        // output row 2g + 2 of image n; row 2g + 1 precedes it (and exists
-        // only when has_a, so da is formed only then)
+        // offset of output row 2g + 2 of image n; row 2g + 1 precedes it and
+        // exists only when has_a, so its address is formed only then
         const size_t off_b = ((size_t)n * 2 * H + (size_t)(2 * g + 2)) * (2 * row_bytes) +
                           (size_t)blockIdx.x * 64 * OUT;
         if (active) {
@@ -717,7 +717,9 @@ __global__ __launch_bounds__(64 * RB) void nearest_up2_u8(
     constexpr int S = Up2Shape<C>::S;
     constexpr int IN = S * C;
     constexpr int OUT = 2 * S * C;
+    // wider chunks go out through LDS; an unstaged chunk is one 16-byte piece
     constexpr bool STAGE = OUT > 16;
+    static_assert(OUT % 16 == 0 && (STAGE || OUT == 16), "chunk shape");
     __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? RB * 64 * OUT : 16];
     const int lane = threadIdx.x;
     const int m = blockIdx.x * 64 + lane;
