@@ -97,6 +97,8 @@ int launch(void (*kernel)(P...), dim3 grid, dim3 block, unsigned lds_bytes, hipS
     return e == hipSuccess ? MI_RESIZE_OK : MI_RESIZE_ERR_HIP;
 }
 
+constexpr bool kDirectStageRgb = true;
+
 template <typename T, int C, int OUT = kOutSame, bool ROI = false>
 int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                           hipStream_t st, const Affine &aff = Affine{},
@@ -111,6 +113,11 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
                       dW, rows, g.rows_per_block, g.col_blocks, aff, rois);
     };
     if (pix4) return go(linear_generic<T, C, C == 4 && OUT == kOutSame, OUT, ROI>);
+    if constexpr (sizeof(T) == 4 && C == 3 && OUT == kOutSame && !ROI) {
+        // float RGB rows that start on 16-byte boundaries: staged stores
+        if (kDirectStageRgb && dW % 4 == 0 && aligned(dst, 16))
+            return go(linear_generic<T, C, false, OUT, ROI, kBorderClamp, true>);
+    }
     return go(linear_generic<T, C, false, OUT, ROI>);
 }
 

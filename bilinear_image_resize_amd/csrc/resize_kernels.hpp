@@ -26,6 +26,19 @@
 namespace mirsz {
 
 constexpr int kBlock = 256;   // 4 wave64 per workgroup
+constexpr bool kDirectNtStores = true;
+// four dwords as a native vector (16-byte loads and stores, non-temporal ones)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Orders this wave's LDS accesses before and after it.  A wave's LDS
+// operations complete in issue order, so keeping the compiler from moving
+// them across this point is all the synchronisation a wave-private slot needs.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // --------------------------------------------------------------------------
 // Coordinate map for one axis.  Output index d of an axis of n_out samples
@@ -227,19 +240,36 @@ __device__ __forceinline__ Crop load_crop(const int32_t *rois, long long n, int 
 // output pixel per row.  PIX4: C == 4 and the buffers are aligned so that a
 // whole pixel moves as one 4-byte (u8) or 16-byte (f32) access.
 // --------------------------------------------------------------------------
+//
+// Stores: a lane's value or 4- or 16-byte pixel is one lane-contiguous
+// store with the non-temporal hint (one-byte values excepted: 64 bytes per
+// instruction are part of a line).  STG (float RGB, output rows 16-byte
+// aligned): each wave's 64 pixels (768 bytes) go through LDS and out as
+// lane-contiguous 16-byte non-temporal stores instead of three strided
+// floats per lane; lanes past the row end then compute on the last
+// column's taps and store nothing.
 template <typename T, int C, bool PIX4, int OUT = kOutSame, bool ROI = false,
-          int BORDER = kBorderClamp>
+          int BORDER = kBorderClamp, bool STG = false>
 __global__ __launch_bounds__(kBlock) void linear_generic(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int col_blocks, Affine aff,
     const int32_t *__restrict__ rois)
 {
+    static_assert(!STG || (sizeof(T) == 4 && C == 3 && OUT == kOutSame && !ROI &&
+                           BORDER == kBorderClamp), "staged stores are for float RGB");
     T *const dst = (T *)dst_v;
     float *const dstf = (float *)dst_v;
+    auto st = [](auto &ref, auto v) {
+        if constexpr (kDirectNtStores && sizeof(v) > 1) __builtin_nontemporal_store(v, &ref);
+        else ref = v;
+    };
+    __shared__ __attribute__((aligned(16))) float stage_all[STG ? kBlock * C : 1];
     const int cb = (int)(blockIdx.x % (unsigned)col_blocks);
     const long long rb = blockIdx.x / (unsigned)col_blocks;
-    const int x = cb * kBlock + (int)threadIdx.x;
-    if (x >= dW) return;
+    const int wave_x0 = cb * kBlock + ((int)threadIdx.x & ~63);   // the wave's first column
+    const int x_lane = cb * kBlock + (int)threadIdx.x;
+    if (STG ? wave_x0 >= dW : x_lane >= dW) return;
+    const int x = STG ? min(x_lane, dW - 1) : x_lane;
 
     long long g = rb * rows_per_block;
     long long g_end = g + rows_per_block;
@@ -284,16 +314,18 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                     o |= blend_u8((a >> s) & 255u, (b >> s) & 255u, (c >> s) & 255u,
                                   (d >> s) & 255u, wx1, wy1) << s;
                 }
-                *(uint32_t *)out = o;
+                st(*(uint32_t *)out, o);
             } else if constexpr (OUT == kOutSame) {
 #pragma unroll
-                for (int k = 0; k < C; ++k)
-                    out[k] = (uint8_t)blend_u8(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k],
-                                               wx1, wy1);
+                for (int k = 0; k < C; ++k) {
+                    const uint8_t v = (uint8_t)blend_u8(r0[xa + k], r0[xb + k], r1[xa + k],
+                                                        r1[xb + k], wx1, wy1);
+                    if constexpr (C == 1) st(out[k], v); else out[k] = v;
+                }
             } else if constexpr (OUT == kOutGrey) {
                 auto gr = [](const T *p) { return grey_u8(p[0], p[1], p[2]); };
-                dst[(size_t)g * dW + x] =
-                    (uint8_t)blend_u8(gr(r0 + xa), gr(r0 + xb), gr(r1 + xa), gr(r1 + xb), wx1, wy1);
+                st(dst[(size_t)g * dW + x],
+                   (uint8_t)blend_u8(gr(r0 + xa), gr(r0 + xb), gr(r1 + xa), gr(r1 + xb), wx1, wy1));
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
@@ -303,7 +335,7 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                     if constexpr (OUT == kOutNormNHWC)
                         dstf[((size_t)g * dW + x) * C + k] = o;
                     else
-                        dstf[(((size_t)n * C + k) * dH + dy) * dW + x] = o;
+                        st(dstf[(((size_t)n * C + k) * dH + dy) * dW + x], o);
                 }
             }
         } else {
@@ -318,15 +350,32 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
                 o.y = blend_f32(a.y, b.y, c.y, d.y, wxf, wyf);
                 o.z = blend_f32(a.z, b.z, c.z, d.z, wxf, wyf);
                 o.w = blend_f32(a.w, b.w, c.w, d.w, wxf, wyf);
-                *(float4 *)out = o;
+                st(*(u32x4_t *)out, __builtin_bit_cast(u32x4_t, o));
             } else if constexpr (OUT == kOutGrey) {
                 auto gr = [](const T *p) { return grey_f32(p[0], p[1], p[2]); };
-                dst[(size_t)g * dW + x] =
-                    blend_f32(gr(r0 + xa), gr(r0 + xb), gr(r1 + xa), gr(r1 + xb), wxf, wyf);
-            } else {
+                st(dst[(size_t)g * dW + x],
+                   blend_f32(gr(r0 + xa), gr(r0 + xb), gr(r1 + xa), gr(r1 + xb), wxf, wyf));
+            } else if constexpr (STG) {
+                float *stage = stage_all + (threadIdx.x & ~63) * C;   // this wave's 64 pixels
 #pragma unroll
                 for (int k = 0; k < C; ++k)
-                    out[k] = blend_f32(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k], wxf, wyf);
+                    stage[(threadIdx.x & 63) * C + k] =
+                        blend_f32(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k], wxf, wyf);
+                wave_sync();
+                // the row segment's bytes: a multiple of 48 (dW % 4 == 0)
+                const int seg_bytes = min(64, dW - wave_x0) * C * 4;
+                const int bb = 16 * (threadIdx.x & 63);
+                if (bb < seg_bytes)
+                    __builtin_nontemporal_store(
+                        *(const u32x4_t *)((const uint8_t *)stage + bb),
+                        (u32x4_t *)((uint8_t *)(dst + ((size_t)g * dW + wave_x0) * C) + bb));
+                wave_sync();
+            } else {
+#pragma unroll
+                for (int k = 0; k < C; ++k) {
+                    const float v = blend_f32(r0[xa + k], r0[xb + k], r1[xa + k], r1[xb + k], wxf, wyf);
+                    if constexpr (C == 1) st(out[k], v); else out[k] = v;
+                }
             }
         }
         if (++dy == dH) {
@@ -367,22 +416,11 @@ template <int C> struct HalfShape { static constexpr int PX = C == 1 ? 16 : 4; }
 
 constexpr int kHalfLanes = 64;
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load_stream(const uint8_t *p)
 {
     const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Orders this wave's LDS accesses before and after it.  A wave's LDS
-// operations complete in issue order, so keeping the compiler from moving
-// them across this point is all the synchronisation a wave-private slot needs.
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Writes one wave's output row segment back to device memory.  The segment
