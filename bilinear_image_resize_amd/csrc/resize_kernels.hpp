@@ -816,17 +816,26 @@ template <> struct CopyUnit<1>  { using type = uint8_t; };
 template <> struct CopyUnit<4>  { using type = uint32_t; };
 template <> struct CopyUnit<16> { using type = uint4; };
 
-template <int BPP, int UNIT>
+// Stores: a whole 4- or 16-byte pixel per lane is one lane-contiguous
+// non-temporal store; STG (12-byte pixels, output rows 16-byte aligned)
+// writes each wave's 64 pixels through LDS as lane-contiguous 16-byte
+// non-temporal stores, as the linear direct kernel does for float RGB.
+template <int BPP, int UNIT, bool STG = false>
 __global__ __launch_bounds__(kBlock) void nearest_generic(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int col_blocks, int map)
 {
     using U = typename CopyUnit<UNIT>::type;
     constexpr int K = BPP / UNIT;
+    static_assert(!STG || (BPP == 12 && UNIT == 4), "staged stores are for 12-byte pixels");
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[STG ? kBlock * BPP : 16];
     const int cb = (int)(blockIdx.x % (unsigned)col_blocks);
     const long long rb = blockIdx.x / (unsigned)col_blocks;
-    const int x = cb * kBlock + (int)threadIdx.x;
-    if (x >= dW) return;
+    const int wave_x0 = cb * kBlock + ((int)threadIdx.x & ~63);   // the wave's first column
+    const int x_lane = cb * kBlock + (int)threadIdx.x;
+    if (STG ? wave_x0 >= dW : x_lane >= dW) return;
+    // lanes past the row end (staged form only) copy the last column, unstored
+    const int x = STG ? min(x_lane, dW - 1) : x_lane;
     const size_t sx = (size_t)nearest_index(x, W, dW, map) * BPP;
 
     long long g = rb * rows_per_block;
@@ -837,9 +846,30 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
     for (; g < g_end; ++g) {
         const int sy = nearest_index(dy, H, dH, map);
         const U *from = (const U *)(src + (((size_t)n * H + sy) * W) * BPP + sx);
-        U *to = (U *)(dst + ((size_t)g * dW + x) * BPP);
+        if constexpr (STG) {
+            uint8_t *stage = stage_all + (threadIdx.x & ~63) * BPP;   // this wave's 64 pixels
 #pragma unroll
-        for (int k = 0; k < K; ++k) to[k] = from[k];
+            for (int k = 0; k < K; ++k) ((U *)(stage + (threadIdx.x & 63) * BPP))[k] = from[k];
+            wave_sync();
+            // the row segment's bytes: a multiple of 48 (dW % 4 == 0)
+            const int seg_bytes = min(64, dW - wave_x0) * BPP;
+            const int bb = 16 * (threadIdx.x & 63);
+            if (bb < seg_bytes)
+                __builtin_nontemporal_store(*(const u32x4_t *)(stage + bb),
+                                            (u32x4_t *)(dst + ((size_t)g * dW + wave_x0) * BPP + bb));
+            wave_sync();
+        } else {
+            U *to = (U *)(dst + ((size_t)g * dW + x) * BPP);
+            if constexpr (K == 1 && UNIT >= 4 && kDirectNtStores) {
+                if constexpr (UNIT == 16)
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, from[0]), (u32x4_t *)to);
+                else
+                    __builtin_nontemporal_store(from[0], to);
+            } else {
+#pragma unroll
+                for (int k = 0; k < K; ++k) to[k] = from[k];
+            }
+        }
         if (++dy == dH) { dy = 0; ++n; }
     }
 }

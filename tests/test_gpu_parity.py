@@ -178,6 +178,29 @@ def test_double_upscale_shapes(C):
                           "up2 %s %s" % (mode, (C, N, H, W)))
 
 
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_rowseg_rgb_enlargements(dtype, monkeypatch):
+    """RGB enlargements forced onto the row-segment kernel (float ones
+    take the direct kernel by default): output widths with rows on 16-byte
+    boundaries and others, several segments per row with a partial last
+    one, batches, and shapes that only just enlarge."""
+    monkeypatch.setenv("MI_RESIZE_PATH", "rowseg")
+    q = 16 if dtype == "u8" else 4
+    r = np.random.default_rng(6060 + (dtype == "f32"))
+    shapes = [(1, 37, 50, 80, 32 * q), (2, 9, 11, 20, 5 * q), (1, 100, 100, 101, 25 * q),
+              (3, 20, 30, 45, 45), (1, 64, 300, 70, 81 * q), (1, 5, 7, 9, 3 * q + 1)]
+    for _ in range(12):
+        N, H, W = int(r.integers(1, 3)), int(r.integers(1, 60)), int(r.integers(1, 300))
+        dH, dW = H + int(r.integers(0, 60)), q * max(1, (W + int(r.integers(1, 200))) // q)
+        shapes.append((N, H, W, dH, dW))
+    for mode in ("linear", "nearest"):
+        for i, (N, H, W, dH, dW) in enumerate(shapes):
+            say("case rowseg rgb enlarge %s %s #%d %s" % (dtype, mode, i, (N, H, W, dH, dW)))
+            s = random_image(r, (N, H, W, 3), dtype)
+            assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
+                          "rowseg rgb enlarge %s %s %s" % (dtype, mode, (N, H, W, dH, dW)))
+
+
 @pytest.mark.parametrize("C", [1, 3, 4])
 def test_double_upscale_random_shapes(C):
     """Seeded random shapes that the exact 2x kernels take (widths a multiple
