@@ -164,6 +164,15 @@ constexpr long long kSegMinBandRowsNarrow = 3;
 // round trip (random crops of the thumbnail batch: 2 rows 44.9 us, 4 rows
 // 40.3 us, 8 rows 43.6 us).
 constexpr long long kSegMinBandRowsRoi = 4;
+// Enlargements (more output rows than source rows) amortise a band's set-up
+// and its staged boundary row over more output rows, down to about 5000
+// bands, within 3..6 rows (us, two-row bands -> this rule: 720p -> 1080p RGB
+// 9.8 -> 9.4; 1080p -> 1620x2880 RGB 16.3 -> 14.7, RGBA 17.4 -> 16.0;
+// 8x300x400 -> 1000x1200 RGB 29.3 -> 24.5; 2000^2 -> 3000^2 float 22.1 ->
+// 17.5; fewer bands than this left too few waves, more rows were slower).
+constexpr long long kSegTargetBandsUp = 5000;
+constexpr long long kSegMinBandRowsUp = 3;
+constexpr long long kSegMaxBandRowsUp = 6;
 // Below this many output pixels the launch is latency-bound and the direct
 // kernels (no staging round trip, no per-lane column table of PX entries)
 // finish first.
@@ -192,7 +201,7 @@ struct SegPlan {
 // columns (taps on both sides plus rounding), plus 15 bytes of misalignment
 // and the slack a two-tap read may run past the last staged pixel.
 bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, long long min_rows,
-                 SegPlan &pl)
+                 bool enlarge, SegPlan &pl)
 {
     const long long cols = (long long)kSegLanes * px;
     long long span = ((cols - 1) * W) / dW + 3;
@@ -202,6 +211,12 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, long lo
     pl.seg_cap = (int)cap;
     const long long gx = (dW + cols - 1) / cols;
     long long rpb = (rows * gx + kSegTargetBands - 1) / kSegTargetBands;
+    if (enlarge) {
+        // about kSegTargetBandsUp bands of kSegMinBandRowsUp..kSegMaxBandRowsUp rows
+        long long up = (rows * gx + kSegTargetBandsUp - 1) / kSegTargetBandsUp;
+        up = up < kSegMinBandRowsUp ? kSegMinBandRowsUp : (up > kSegMaxBandRowsUp ? kSegMaxBandRowsUp : up);
+        if (rpb < up) rpb = up;
+    }
     if (rpb < min_rows) rpb = min_rows;
     pl.rows_per_block = (int)rpb;
     const long long bands = (rows + rpb - 1) / rpb;
@@ -222,7 +237,9 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
         OUT == kOutGrey ? (int)sizeof(T) : (OUT == kOutSame ? C * (int)sizeof(T) : 4 * C);
     const long long min_rows = ROI ? kSegMinBandRowsRoi
                                    : (out_px_bytes == 1 ? kSegMinBandRowsNarrow : kSegMinBandRows);
-    if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, min_rows, pl))
+    // crops are sized against their own regions, so only whole images count
+    const bool enlarge = !ROI && dH > H;
+    if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, min_rows, enlarge, pl))
         return false;
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8;
     // a slot then holds 64 lanes x that many chunks (the kernel writes its
