@@ -164,7 +164,7 @@ constexpr long long kSegMinBandRowsNarrow = 3;
 // round trip (random crops of the thumbnail batch: 2 rows 44.9 us, 4 rows
 // 40.3 us, 8 rows 43.6 us).
 constexpr long long kSegMinBandRowsRoi = 4;
-// Enlargements (more output rows than source rows) amortise a band's set-up
+// Enlargements (more output pixels than source pixels) amortise a band's set-up
 // and its staged boundary row over more output rows, down to about 5000
 // bands, within 3..6 rows (us, two-row bands -> this rule: 720p -> 1080p RGB
 // 9.8 -> 9.4; 1080p -> 1620x2880 RGB 16.3 -> 14.7, RGBA 17.4 -> 16.0;
@@ -237,8 +237,11 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
         OUT == kOutGrey ? (int)sizeof(T) : (OUT == kOutSame ? C * (int)sizeof(T) : 4 * C);
     const long long min_rows = ROI ? kSegMinBandRowsRoi
                                    : (out_px_bytes == 1 ? kSegMinBandRowsNarrow : kSegMinBandRows);
-    // crops are sized against their own regions, so only whole images count
-    const bool enlarge = !ROI && dH > H;
+    // the output outweighs the source (pixel counts: rgbaf enlarges its
+    // rows but halves its columns and is bandwidth-bound, 154.5 us with
+    // five-row bands, 161.4 with six); crops are sized against their own
+    // regions, so only whole images count
+    const bool enlarge = !ROI && (long long)dH * dW > (long long)H * W;
     if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, min_rows, enlarge, pl))
         return false;
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8;
