@@ -201,6 +201,27 @@ def test_rowseg_rgb_enlargements(dtype, monkeypatch):
                           "rowseg rgb enlarge %s %s %s" % (dtype, mode, (N, H, W, dH, dW)))
 
 
+@pytest.mark.parametrize("C", [3, 4])
+def test_direct_float_enlargements(C):
+    """Float RGB / RGBA enlargements take the direct kernels: whole 16-byte
+    pixels (RGBA) stored with the non-temporal hint, and RGB rows that start
+    on 16-byte boundaries (widths a multiple of 4) written through LDS as
+    16-byte pieces; other RGB widths store three floats per lane.  Widths
+    leave partial last waves and workgroups; linear and nearest."""
+    r = np.random.default_rng(7070 + C)
+    shapes = [(1, 30, 40, 45, 64), (1, 30, 40, 45, 68), (2, 17, 33, 40, 100), (1, 9, 50, 13, 257),
+              (3, 5, 7, 11, 12), (1, 64, 64, 96, 256), (1, 2, 3, 3, 4)]
+    for _ in range(10):
+        N, H, W = int(r.integers(1, 3)), int(r.integers(1, 50)), int(r.integers(1, 300))
+        shapes.append((N, H, W, H + int(r.integers(0, 50)), W + int(r.integers(1, 300))))
+    for mode in ("linear", "nearest"):
+        for i, (N, H, W, dH, dW) in enumerate(shapes):
+            say("case direct float enlarge C=%d %s #%d %s" % (C, mode, i, (N, H, W, dH, dW)))
+            s = random_image(r, (N, H, W, C), "f32")
+            assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
+                          "direct float enlarge C=%d %s %s" % (C, mode, (N, H, W, dH, dW)))
+
+
 @pytest.mark.parametrize("C", [1, 3, 4])
 def test_double_upscale_random_shapes(C):
     """Seeded random shapes that the exact 2x kernels take (widths a multiple
