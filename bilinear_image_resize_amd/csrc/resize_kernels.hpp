@@ -26,6 +26,8 @@
 namespace mirsz {
 
 constexpr int kBlock = 256;   // 4 wave64 per workgroup
+// The direct kernels' lane-contiguous stores carry the non-temporal hint
+// (their output is never read back; float RGBA 1080p -> 2x 51.7 -> 29.9 us).
 constexpr bool kDirectNtStores = true;
 // four dwords as a native vector (16-byte loads and stores, non-temporal ones)
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
