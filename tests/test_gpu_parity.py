@@ -250,6 +250,9 @@ EDGE = [
     (7, 31, 33, 3, 61, 67), (1, 1000, 10, 1, 3, 999),
     (1, 4, 4000, 3, 2, 37), (1, 3, 5000, 4, 3, 7), (2, 9, 1025, 1, 5, 1023), (1, 5, 1024, 1, 7, 1025),
     (1, 6, 257, 3, 4, 255), (3, 17, 129, 4, 9, 131),
+    # the widest rows of the exact 2x and 2:1 kernels (uint8) and of the
+    # float RGB rows staged through LDS on the direct kernels
+    (1, 2, 32760, 1, 4, 65520), (1, 4, 65504, 3, 2, 32752), (1, 2, 20000, 3, 3, 65532),
 ]
 
 
