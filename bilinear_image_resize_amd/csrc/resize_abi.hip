@@ -258,7 +258,10 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const int slot_bytes = pl.seg_cap + (B == kBorderWrap ? 32 : 0);
     if (2 * slot_bytes > kSegLdsBudget) return false;
     auto go = [&](auto kernel) {
-        return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), kSegWaves * 2 * slot_bytes, st,
+        constexpr int nstage = seg_nhwc_stage_bytes<T, C, OUT>();
+        const int lds_bytes = kSegWaves * (2 * slot_bytes +
+                                           (nstage > 0 && seg_nhwc_staged(dst, dW, C) ? nstage : 0));
+        return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), lds_bytes, st,
                       (const T *)src, dst,
                       H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
                       (long long)batch * H * W * C, aff, rois, nn_map);

@@ -1146,6 +1146,22 @@ __device__ __forceinline__ void border_taps(int q, int r, int den, int n, int &a
     }
 }
 
+// Normalised NHWC output of the row-segment kernel: each lane's PX C floats
+// would go out as strided 16-byte pieces, so where output rows start on
+// 16-byte boundaries each wave's row segment goes through LDS (64 PX C
+// floats per wave, after all waves' slots) and out as lane-contiguous
+// 16-byte non-temporal stores.  Compile-time: only this output stage has
+// the code and the LDS.
+template <typename T, int C, int OUT>
+__host__ __device__ constexpr int seg_nhwc_stage_bytes()
+{
+    return OUT == kOutNormNHWC ? kSegLanes * SegShape<T, C>::PX * C * 4 : 0;
+}
+__host__ __device__ inline bool seg_nhwc_staged(const void *dst, int dW, int C)
+{
+    return ((uintptr_t)dst & 15) == 0 && ((size_t)dW * C * 4) % 16 == 0;
+}
+
 template <typename T, int C, bool NEAREST, int KMAX, bool NT, int OUT = kOutSame, bool ROI = false,
           int B = kBorderClamp>
 __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
@@ -1169,6 +1185,10 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     // wave index, made visibly uniform so that all per-row planning stays scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kSegLanes);
     uint8_t *const lds = lds_all + (size_t)wave * 2 * slot_bytes;   // this wave's two slots
+    constexpr int NSTAGE = seg_nhwc_stage_bytes<T, C, OUT>();
+    [[maybe_unused]] const bool nstaged = NSTAGE > 0 && seg_nhwc_staged(dst_v, dW, C);
+    [[maybe_unused]] uint8_t *const lds_n =
+        lds_all + (size_t)kSegWaves * 2 * slot_bytes + (size_t)wave * NSTAGE;
     const int wx0 = blockIdx.x * kSegLanes * PX;  // first output column of the segment
     const int wx1 = min(wx0 + kSegLanes * PX, dW) - 1;
     const int x0 = wx0 + lane * PX;               // this lane's first output column
@@ -1515,7 +1535,17 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                     f[k] = fmaf((float)res[k], aff.scale[k % C], aff.bias[k % C]);
                 float *dstf = (float *)dst_v;
                 if constexpr (OUT == kOutNormNHWC) {
-                    store_chunk<float, PX * C>(dstf + ((size_t)g * dW + x0) * C, f, valid_px * C);
+                    if (nstaged) {
+#pragma unroll
+                        for (int k = 0; k < PX * C / 4; ++k) {
+                            u32x4_t q;
+                            __builtin_memcpy(&q, f + 4 * k, 16);
+                            *(u32x4_t *)(lds_n + lane * PX * C * 4 + 16 * k) = q;
+                        }
+                    } else {
+                        store_chunk<float, PX * C>(dstf + ((size_t)g * dW + x0) * C, f,
+                                                   valid_px * C);
+                    }
                 } else {
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
@@ -1525,6 +1555,22 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                         store_chunk<float, PX>(dstf + (((size_t)n * C + c) * dH + dy) * dW + x0,
                                                plane, valid_px);
                     }
+                }
+            }
+        }
+        if constexpr (NSTAGE > 0) {
+            if (nstaged) {
+                // the segment's bytes: a multiple of 16, since dW C 4 and
+                // the segment's start both are
+                wave_sync();
+                const int seg_bytes = (wx1 - wx0 + 1) * C * 4;
+                uint8_t *o = (uint8_t *)((float *)dst_v + ((size_t)g * dW + wx0) * C);
+#pragma unroll
+                for (int k = 0; k < (NSTAGE + 1023) / 1024; ++k) {
+                    const int bb = 1024 * k + 16 * lane;
+                    if (bb < seg_bytes)
+                        __builtin_nontemporal_store(*(const u32x4_t *)(lds_n + bb),
+                                                    (u32x4_t *)(o + bb));
                 }
             }
         }
