@@ -1146,6 +1146,7 @@ __device__ __forceinline__ void border_taps(int q, int r, int den, int n, int &a
     }
 }
 
+constexpr bool kSegStageFloatRgb = true;
 // Normalised NHWC output of the row-segment kernel: each lane's PX C floats
 // would go out as strided 16-byte pieces, so where output rows start on
 // 16-byte boundaries each wave's row segment goes through LDS (64 PX C
@@ -1155,7 +1156,9 @@ __device__ __forceinline__ void border_taps(int q, int r, int den, int n, int &a
 template <typename T, int C, int OUT>
 __host__ __device__ constexpr int seg_nhwc_stage_bytes()
 {
-    return OUT == kOutNormNHWC ? kSegLanes * SegShape<T, C>::PX * C * 4 : 0;
+    return OUT == kOutNormNHWC || (kSegStageFloatRgb && OUT == kOutSame && sizeof(T) == 4 && C == 3)
+               ? kSegLanes * SegShape<T, C>::PX * C * 4
+               : 0;
 }
 __host__ __device__ inline bool seg_nhwc_staged(const void *dst, int dW, int C)
 {
@@ -1524,7 +1527,18 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             }
         }
         if (valid_px > 0) {
-            if constexpr (OUT == kOutSame) {
+            if constexpr (OUT == kOutSame && NSTAGE > 0) {
+                if (nstaged) {
+#pragma unroll
+                    for (int k = 0; k < PX * C / 4; ++k) {
+                        u32x4_t q;
+                        __builtin_memcpy(&q, (const float *)res + 4 * k, 16);
+                        *(u32x4_t *)(lds_n + lane * PX * C * 4 + 16 * k) = q;
+                    }
+                } else {
+                    store_chunk<T, PX * C>(out_lane + (size_t)g * dW * C, res, valid_px * C);
+                }
+            } else if constexpr (OUT == kOutSame) {
                 store_chunk<T, PX * C>(out_lane + (size_t)g * dW * C, res, valid_px * C);
             } else if constexpr (OUT == kOutGrey) {
                 store_chunk<T, PX>(dst + (size_t)g * dW + x0, resg, valid_px);
