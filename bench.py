@@ -57,9 +57,12 @@ def parse():
     p.add_argument("--workload", default="4k")
     p.add_argument("--mode", default=None, help="linear (default) or nearest")
     p.add_argument("--op", default="resize", choices=["resize", "normalize", "crop", "grey"],
-                   help="normalize: the fused uint8 -> float32 NCHW resize + normalisation "
+                   help="normalize: the fused uint8 -> float32 resize + normalisation (NCHW, or "
+                        "NHWC with --layout nhwc) "
                         "(ImageNet mean / std, alpha 1/255) on the same workload; crop: "
                         "batched crop-then-resize with seeded random-resized-crop regions")
+    p.add_argument("--layout", default="nchw", choices=["nchw", "nhwc"],
+                   help="output layout of --op normalize")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="reuse one buffer pair (cache-resident)")
@@ -277,7 +280,7 @@ def main():
     if fused:
         if w.dtype != "u8" or mode != "linear":
             sys.exit("--op normalize needs a uint8 linear workload")
-        dst_shape = (w.batch, w.C, w.dH, w.dW)
+        dst_shape = (w.batch, w.C, w.dH, w.dW) if args.layout == "nchw" else (w.batch, w.dH, w.dW, w.C)
         dst_bytes = w.dst_pixels * w.C * 4
         tdt_out = torch.float32
     elif grey:
@@ -306,9 +309,10 @@ def main():
         fa = ctypes.c_float * 4
         mean_c, std_c = fa(0.485, 0.456, 0.406, 0.5), fa(0.229, 0.224, 0.225, 0.25)
         base = lib.resize_linear_normalize
+        layout_code = R.LAYOUTS[args.layout.upper()]
 
         def entry(s_, d_, N_, H_, W_, C_, code_, dH_, dW_, sh_):
-            return base(s_, d_, N_, H_, W_, C_, dH_, dW_, 1.0 / 255.0, mean_c, std_c, 1, sh_)
+            return base(s_, d_, N_, H_, W_, C_, dH_, dW_, 1.0 / 255.0, mean_c, std_c, layout_code, sh_)
     if grey:
         entry = lib.resize_linear_grey
     if args.border != "clamp":
@@ -431,7 +435,7 @@ def main():
             ok = np.array_equal(got, ref) if w.dtype == "u8" else float(np.abs(got - ref).max()) <= 1e-5
         elif fused:
             ref = oracle.resize_linear_normalize(src_np, w.dH, w.dW, 1 / 255, (0.485, 0.456, 0.406, 0.5)[:w.C],
-                                                 (0.229, 0.224, 0.225, 0.25)[:w.C], "NCHW")
+                                                 (0.229, 0.224, 0.225, 0.25)[:w.C], args.layout.upper())
             ok = bool((np.abs(got - ref) <= 1e-5 * np.maximum(1.0, np.abs(ref))).all())
         else:
             if mode == "linear":
@@ -460,7 +464,7 @@ def main():
         "config": {
             "workload": "%s: %s %dx%dx%dx%d -> %dx%d %s%s" % (
                 w.name, w.dtype, w.batch, w.H, w.W, w.C, w.dH, w.dW, mode,
-                " + normalize to f32 NCHW" if fused else (" of random crops" if cropped else
+                " + normalize to f32 " + args.layout.upper() if fused else (" of random crops" if cropped else
                 " to grey" if grey else
                 ("" if args.border == "clamp" else ", %s border" % args.border))),
             "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
