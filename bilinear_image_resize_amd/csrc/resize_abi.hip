@@ -259,6 +259,9 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     if (2 * slot_bytes > kSegLdsBudget) return false;
     auto go = [&](auto kernel) {
         constexpr int nstage = seg_nhwc_stage_bytes<T, C, OUT>();
+        // at most 4 x (16 KiB of slots + 4 KiB of output staging) = 80 KiB,
+        // within the 160 KiB one gfx950 workgroup may use
+        static_assert(kSegWaves * (kSegLdsBudget + nstage) <= 160 * 1024, "LDS per workgroup");
         const int lds_bytes = kSegWaves * (2 * slot_bytes +
                                            (nstage > 0 && seg_nhwc_staged(dst, dW, C) ? nstage : 0));
         return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), lds_bytes, st,
