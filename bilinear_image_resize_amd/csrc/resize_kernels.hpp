@@ -453,7 +453,9 @@ __device__ __forceinline__ void store_staged(const uint8_t *lds, uint8_t *out, i
 // (RGB: 12 bytes) are stored as dwords with no hint.  Measured on the 4K RGB
 // frame: staging the 12-byte results through LDS for whole-line
 // non-temporal stores 6.7 -> 8.3 us, two or four waves per workgroup 6.7 ->
-// 6.85 us; non-temporal 16-byte stores for grey 4K -> 1080p 4.01 -> 3.88 us.
+// 6.85 us, the non-temporal hint on the 12-byte stores 6.54 -> 6.74 us
+// (though 5% faster on a 16 x 480x640 batch); non-temporal 16-byte stores
+// for grey 4K -> 1080p 4.01 -> 3.88 us.
 template <int C, bool GREY = false>
 __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows)
