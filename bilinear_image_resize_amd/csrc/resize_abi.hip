@@ -125,15 +125,34 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
 }
 
 constexpr long long kMaxGridY = 65535;
+// x extents stay well inside HIP's limit of 2^32 threads per dimension
+constexpr long long kMaxGridX = 1LL << 24;
 
 template <int C, bool GREY = false>
 int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStream_t st)
 {
     constexpr int seg = kHalfLanes * HalfShape<C>::PX;
     const long long rows = (long long)batch * dH;
-    const dim3 grid((dW + seg - 1) / seg, (unsigned)(rows < kMaxGridY ? rows : kMaxGridY));
-    return launch(linear_half_u8<C, GREY>, grid, dim3(kHalfLanes), 0, st, (const uint8_t *)src,
-                  (uint8_t *)dst, dW, rows);
+    const long long segs = (dW + seg - 1) / seg;
+    // one or two segments per row: rows along x (see the kernel)
+    if (segs <= 2) {
+        const dim3 grid((unsigned)(rows < kMaxGridX ? rows : kMaxGridX), (unsigned)segs);
+        return launch(linear_half_u8<C, GREY, true>, grid, dim3(kHalfLanes), 0, st,
+                      (const uint8_t *)src, (uint8_t *)dst, dW, rows, 0ULL, 0);
+    }
+    // The kernel numbers workgroups below 2^31 and splits a number n into
+    // row and segment as n / segs = (n * magic) >> shift, with
+    // shift = 31 + ceil(log2 segs) and magic = floor(2^shift / segs) + 1:
+    // exact for every n < 2^31 (the round-up method for 31-bit dividends).
+    long long gy = rows < kMaxGridY ? rows : kMaxGridY;
+    if (segs * gy > 0x7fffffffLL) gy = 0x7fffffffLL / segs;
+    int lg = 0;
+    while ((1LL << lg) < segs) ++lg;
+    const int shift = 31 + lg;
+    const unsigned long long magic = (1ULL << shift) / (unsigned long long)segs + 1;
+    return launch(linear_half_u8<C, GREY, false>, dim3((unsigned)segs, (unsigned)gy),
+                  dim3(kHalfLanes), 0, st, (const uint8_t *)src, (uint8_t *)dst, dW, rows, magic,
+                  shift);
 }
 
 // Exact 2:1 uint8 downscale whose rows split into whole 16-byte chunks and

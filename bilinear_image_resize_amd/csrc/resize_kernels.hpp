@@ -410,9 +410,21 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // beats lanes that load their own (strided) bytes directly by about 8 %, and
 // matches a plain kernel with the same 4:1 read / write byte mix.
 // Needs dW % (C == 1 ? 16 : C == 3 ? 8 : 4) == 0 and 16-byte aligned src /
-// dst, so every row and every 16-byte chunk is aligned.  Grid: x = segments
-// of a row, y = output rows (stride gridDim.y).  Output row g reads source
-// rows 2g and 2g + 1 of the flattened N * H rows, because H = 2 dH.
+// dst, so every row and every 16-byte chunk is aligned.  Output row g reads
+// source rows 2g and 2g + 1 of the flattened N * H rows, because H = 2 dH.
+//
+// Two grid layouts.  Rows of one or two segments (small frames in a batch)
+// use seg_major: x = output rows (stride gridDim.x), y = segment; a grid
+// that is 1 or 2 workgroups wide and thousands tall dispatches markedly
+// slower than the same workgroups laid along x (64 x 224x224 RGB: 5.28 ->
+// 4.08 us; 16 x 640x480 RGB: 5.82 -> 4.89 us, where the full first
+// segments of all rows also go out before the short second ones).  Wider
+// rows keep x = segment, y = output rows (stride gridDim.y) with the XCD
+// renumbering below (4K RGB 6.50 -> 6.40 us, 4K RGBA 8.38 -> 8.21 us,
+// 8 x 1080p RGB 11.10 -> 10.89 us); there the segment-major order is slower
+// (4K RGBA 8.71 us), and so is a one-dimensional grid (4K RGB 6.82 us
+// without the renumbering, 6.54 with it).  Eight pixels per lane instead of
+// four (RGB, RGBA) measured slower on the 4K frames (RGB 6.52 -> 6.97 us).
 // --------------------------------------------------------------------------
 template <int C> struct HalfShape { static constexpr int PX = C == 1 ? 16 : 4; };
 
@@ -456,9 +468,10 @@ __device__ __forceinline__ void store_staged(const uint8_t *lds, uint8_t *out, i
 // 6.85 us, the non-temporal hint on the 12-byte stores 6.54 -> 6.74 us
 // (though 5% faster on a 16 x 480x640 batch); non-temporal 16-byte stores
 // for grey 4K -> 1080p 4.01 -> 3.88 us.
-template <int C, bool GREY = false>
+template <int C, bool GREY, bool SEG_MAJOR>
 __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
-    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows)
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows,
+    unsigned long long seg_magic, int seg_shift)
 {
     static_assert(!GREY || C >= 3, "grey needs RGB(A)");
     constexpr int PX = HalfShape<C>::PX;
@@ -471,14 +484,33 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SRC_B];
 
     const int lane = threadIdx.x;
-    const int seg = blockIdx.x;
+    int seg;
+    long long g, g_step;
+    if constexpr (SEG_MAJOR) {
+        seg = blockIdx.y;
+        g = blockIdx.x;
+        g_step = gridDim.x;
+    } else {
+        // Workgroups go to the 8 XCDs round-robin by linear id.  Renumber
+        // them so each XCD takes one contiguous run of (row, segment)
+        // pairs, row-major: with whole rows in every run, a ragged last
+        // segment no longer lands on the same XCDs every time.  The split
+        // of the new id into row and segment divides by gridDim.x with the
+        // host's multiply-shift pair (exact below 2^31).
+        const unsigned gx = gridDim.x, nwg = gx * gridDim.y;
+        const unsigned lin = blockIdx.y * gx + blockIdx.x, xcd = lin & 7;
+        const unsigned wid = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (lin >> 3);
+        const unsigned row = (unsigned)((wid * seg_magic) >> seg_shift);
+        seg = (int)(wid - row * gx);
+        g = row;
+        g_step = gridDim.y;
+    }
     const int seg_px = min(SEG, dW - seg * SEG);
     const int n16 = seg_px * 2 * C / 16;          // whole: dW meets the divisibility rule
     const size_t src_row = (size_t)2 * dW * C;
     const size_t dst_row = (size_t)dW * OC;
-    // the grid's y extent never exceeds rows, so every workgroup has a
+    // the grid's row extent never exceeds rows, so every workgroup has a
     // first row: a do-while lets all arguments load at once
-    long long g = blockIdx.y;
     do {
         const uint8_t *s0 = src + (size_t)(2 * g) * src_row + (size_t)seg * SRC_B;
         const uint8_t *s1 = s0 + src_row;
@@ -573,7 +605,7 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
             }
         }
         wave_sync();
-        g += gridDim.y;
+        g += g_step;
     } while (g < rows);
 }
 
