@@ -127,6 +127,8 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
 constexpr long long kMaxGridY = 65535;
 // x extents stay well inside HIP's limit of 2^32 threads per dimension
 constexpr long long kMaxGridX = 1LL << 24;
+// workgroups of a grid whose kernel renumbers them (xcd_contiguous, div_by)
+constexpr long long kMaxGroups = 0x7fffffffLL;
 
 template <int C, bool GREY = false>
 int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStream_t st)
@@ -138,21 +140,14 @@ int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStr
     if (segs <= 2) {
         const dim3 grid((unsigned)(rows < kMaxGridX ? rows : kMaxGridX), (unsigned)segs);
         return launch(linear_half_u8<C, GREY, true>, grid, dim3(kHalfLanes), 0, st,
-                      (const uint8_t *)src, (uint8_t *)dst, dW, rows, 0ULL, 0);
+                      (const uint8_t *)src, (uint8_t *)dst, dW, rows, DivBy{});
     }
-    // The kernel numbers workgroups below 2^31 and splits a number n into
-    // row and segment as n / segs = (n * magic) >> shift, with
-    // shift = 31 + ceil(log2 segs) and magic = floor(2^shift / segs) + 1:
-    // exact for every n < 2^31 (the round-up method for 31-bit dividends).
+    // workgroup numbers stay below 2^31 for the kernel's divide by segs
     long long gy = rows < kMaxGridY ? rows : kMaxGridY;
-    if (segs * gy > 0x7fffffffLL) gy = 0x7fffffffLL / segs;
-    int lg = 0;
-    while ((1LL << lg) < segs) ++lg;
-    const int shift = 31 + lg;
-    const unsigned long long magic = (1ULL << shift) / (unsigned long long)segs + 1;
+    if (segs * gy > kMaxGroups) gy = kMaxGroups / segs;
     return launch(linear_half_u8<C, GREY, false>, dim3((unsigned)segs, (unsigned)gy),
-                  dim3(kHalfLanes), 0, st, (const uint8_t *)src, (uint8_t *)dst, dW, rows, magic,
-                  shift);
+                  dim3(kHalfLanes), 0, st, (const uint8_t *)src, (uint8_t *)dst, dW, rows,
+                  make_div_by((unsigned)segs));
 }
 
 // Exact 2:1 uint8 downscale whose rows split into whole 16-byte chunks and
@@ -328,17 +323,28 @@ int launch_up2_u8(const void *src, void *dst, int batch, int H, int W, hipStream
     constexpr int RB = NEAREST ? kUp2RowsNearest<C> : kUp2RowsLinear<C>;
     if constexpr (NEAREST) {
         const long long rows = (long long)batch * H;
+        const long long gx = (chunks_per_row + 63) / 64;
         const long long gy = (rows + RB - 1) / RB;
-        const dim3 grid((chunks_per_row + 63) / 64, (unsigned)(gy < kMaxGridY ? gy : kMaxGridY));
-        return launch(nearest_up2_u8<C, RB>, grid, dim3(64, RB), 0, st,
-                      (const uint8_t *)src, (uint8_t *)dst, W, rows, chunks_per_row);
+        // segment-major for one segment per row, or two with a short second
+        // (see the kernel)
+        if (gx == 1 || (gx == 2 && chunks_per_row - 64 <= 32))
+            return launch(nearest_up2_u8<C, RB, true>,
+                          dim3((unsigned)(gy < kMaxGridX ? gy : kMaxGridX), (unsigned)gx),
+                          dim3(64, RB), 0, st, (const uint8_t *)src, (uint8_t *)dst, W, rows,
+                          chunks_per_row);
+        return launch(nearest_up2_u8<C, RB, false>,
+                      dim3((unsigned)gx, (unsigned)(gy < kMaxGridY ? gy : kMaxGridY)),
+                      dim3(64, RB), 0, st, (const uint8_t *)src, (uint8_t *)dst, W, rows,
+                      chunks_per_row);
     } else {
         // H + 1 gaps per image (H <= 32767 since dH <= 65535); images
         // beyond the grid's z extent are strided
-        const dim3 grid((chunks_per_row + 63) / 64, (unsigned)((H + RB) / RB),
-                        (unsigned)(batch < kMaxGridY ? batch : kMaxGridY));
-        return launch(linear_up2_u8<C, RB>, grid, dim3(64, RB), 0, st,
-                      (const uint8_t *)src, (uint8_t *)dst, H, W, batch, chunks_per_row);
+        const long long gx = (chunks_per_row + 63) / 64, gy = (H + RB) / RB;
+        long long gz = batch < kMaxGridY ? batch : kMaxGridY;
+        if (gx * gy * gz > kMaxGroups) gz = kMaxGroups / (gx * gy);
+        return launch(linear_up2_u8<C, RB>, dim3((unsigned)gx, (unsigned)gy, (unsigned)gz),
+                      dim3(64, RB), 0, st, (const uint8_t *)src, (uint8_t *)dst, H, W, batch,
+                      chunks_per_row, make_div_by((unsigned)gx), make_div_by((unsigned)gy));
     }
 }
 

@@ -42,6 +42,38 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Division by a launch-time constant d >= 1 as a multiply and a shift, for
+// dividends below 2^31 (the round-up method: shift = 31 + ceil(log2 d),
+// magic = floor(2^shift / d) + 1; exact for every such dividend).  Built on
+// the host, passed by value.
+struct DivBy {
+    unsigned long long magic;
+    int shift;
+};
+
+inline DivBy make_div_by(unsigned d)
+{
+    int lg = 0;
+    while ((1ULL << lg) < d) ++lg;
+    return DivBy{(1ULL << (31 + lg)) / d + 1, 31 + lg};
+}
+
+__device__ __forceinline__ unsigned div_by(unsigned n, DivBy d)
+{
+    return (unsigned)((n * d.magic) >> d.shift);
+}
+
+// Workgroups reach the 8 XCDs round-robin by linear id.  This renumbers
+// workgroup lin of nwg so that each XCD takes one contiguous run of ids
+// (XCD k the k-th run): where the work per workgroup repeats with the grid's
+// x extent (a short last segment of every row), whole rows then share out
+// evenly, and neighbouring rows stay on one XCD.
+__device__ __forceinline__ unsigned xcd_contiguous(unsigned lin, unsigned nwg)
+{
+    const unsigned xcd = lin & 7;
+    return xcd * (nwg >> 3) + min(xcd, nwg & 7) + (lin >> 3);
+}
+
 // --------------------------------------------------------------------------
 // Coordinate map for one axis.  Output index d of an axis of n_out samples
 // taken from n_in samples: x = (d + 1/2) n_in / n_out - 1/2 = num / den with
@@ -471,7 +503,7 @@ __device__ __forceinline__ void store_staged(const uint8_t *lds, uint8_t *out, i
 template <int C, bool GREY, bool SEG_MAJOR>
 __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows,
-    unsigned long long seg_magic, int seg_shift)
+    DivBy by_segs)
 {
     static_assert(!GREY || C >= 3, "grey needs RGB(A)");
     constexpr int PX = HalfShape<C>::PX;
@@ -491,16 +523,10 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
         g = blockIdx.x;
         g_step = gridDim.x;
     } else {
-        // Workgroups go to the 8 XCDs round-robin by linear id.  Renumber
-        // them so each XCD takes one contiguous run of (row, segment)
-        // pairs, row-major: with whole rows in every run, a ragged last
-        // segment no longer lands on the same XCDs every time.  The split
-        // of the new id into row and segment divides by gridDim.x with the
-        // host's multiply-shift pair (exact below 2^31).
-        const unsigned gx = gridDim.x, nwg = gx * gridDim.y;
-        const unsigned lin = blockIdx.y * gx + blockIdx.x, xcd = lin & 7;
-        const unsigned wid = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (lin >> 3);
-        const unsigned row = (unsigned)((wid * seg_magic) >> seg_shift);
+        // each XCD takes a contiguous run of (row, segment) pairs
+        const unsigned gx = gridDim.x;
+        const unsigned wid = xcd_contiguous(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
+        const unsigned row = div_by(wid, by_segs);
         seg = (int)(wid - row * gx);
         g = row;
         g_step = gridDim.y;
@@ -680,7 +706,7 @@ __device__ __forceinline__ uint32_t up2_pick(const uint32_t (&e)[ND], int k)
 template <int C, int RB>
 __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
-    int batch, int chunks_per_row)
+    int batch, int chunks_per_row, DivBy by_gx, DivBy by_gy)
 {
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     constexpr int S = Up2LinShape<C>::S;
@@ -694,8 +720,16 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
     constexpr bool STAGE = OUT > 16;       // wider chunks go out through LDS
     __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? RB * 2 * 64 * OUT : 16];
     const int lane = threadIdx.x;
-    const int m = blockIdx.x * 64 + lane;
-    const int g = (int)(blockIdx.y * RB + threadIdx.y) - 1;   // gap, uniform across the wave
+    // (segment, gap group, image) of this workgroup, XCD-contiguous
+    const unsigned gx = gridDim.x, gy = gridDim.y;
+    const unsigned wid = xcd_contiguous((blockIdx.z * gy + blockIdx.y) * gx + blockIdx.x,
+                                        gx * gy * gridDim.z);
+    const unsigned yz = div_by(wid, by_gx);
+    const unsigned bx = wid - yz * gx;
+    const unsigned bz = gridDim.z == 1 ? 0u : div_by(yz, by_gy);
+    const unsigned by = yz - bz * gy;
+    const int m = bx * 64 + lane;
+    const int g = (int)(by * RB + threadIdx.y) - 1;   // gap, uniform across the wave
     const bool active = m < chunks_per_row;
     if (g >= H || (!STAGE && !active)) return;
     const size_t row_bytes = (size_t)W * C;
@@ -732,13 +766,13 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
                                      __builtin_bit_cast(uint32_t, z0), 0x07050301u);
     };
     uint8_t *lds0 = lds_all + threadIdx.y * 2 * 64 * OUT, *lds1 = lds0 + 64 * OUT;
-    const int seg_bytes = min(64, chunks_per_row - (int)blockIdx.x * 64) * OUT;
-    for (int n = blockIdx.z; n < batch; n += gridDim.z) {
+    const int seg_bytes = min(64, chunks_per_row - (int)bx * 64) * OUT;
+    for (int n = bz; n < batch; n += gridDim.z) {
         const uint8_t *img = src + (size_t)n * H * row_bytes;
         // offset of output row 2g + 2 of image n; row 2g + 1 precedes it and
         // exists only when has_a, so its address is formed only then
         const size_t off_b = ((size_t)n * 2 * H + (size_t)(2 * g + 2)) * (2 * row_bytes) +
-                          (size_t)blockIdx.x * 64 * OUT;
+                          (size_t)bx * 64 * OUT;
         if (active) {
             u16x2 ha[NP], hb[NP];
             hsum(img + (size_t)ra * row_bytes, ha);
@@ -779,11 +813,19 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
 // coordinate of output column d is floor((2d + 1) / 4) = d / 2, so the
 // output is every source pixel repeated twice in both directions.  A lane
 // reads S pixels of source row j and writes them doubled to output rows 2j
-// and 2j + 1.  Same shape rules, workgroup and stores as linear_up2_u8; the
-// grid's y runs over groups of RB rows of all N H source rows (strided
-// past the grid's extent).
+// and 2j + 1.  Same shape rules, workgroup and stores as linear_up2_u8.
+// Grid: x = 64-chunk segments, y = groups of RB rows of all N H source rows
+// (strided past the grid's extent); SEG_MAJOR swaps the two.  The launcher
+// takes SEG_MAJOR for rows of one segment (a grid 1 wide and thousands tall
+// dispatches slowly: 64 x 112x112 grey 3.34 -> 2.86 us) and for two
+// segments whose second is at most half full, which the round-robin spread
+// of workgroups over the XCDs would hand to the same four XCDs (4 x 720p
+// grey, 64 + 16 chunks: 4.83 -> 3.85 us).  Otherwise the plain order stays:
+// with a nearly full second segment (1080p -> 4K RGB, 64 + 56 chunks) both
+// the segment-major grid and the XCD-contiguous renumbering the linear
+// kernel uses measured slower (5.69 -> 5.93 us).
 // --------------------------------------------------------------------------
-template <int C, int RB>
+template <int C, int RB, bool SEG_MAJOR>
 __global__ __launch_bounds__(64 * RB) void nearest_up2_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int W, long long rows,
     int chunks_per_row)
@@ -796,17 +838,20 @@ __global__ __launch_bounds__(64 * RB) void nearest_up2_u8(
     static_assert(OUT % 16 == 0 && (STAGE || OUT == 16), "chunk shape");
     __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? RB * 64 * OUT : 16];
     const int lane = threadIdx.x;
-    const int m = blockIdx.x * 64 + lane;
+    // (segment, row group) of this workgroup
+    const unsigned bx = SEG_MAJOR ? blockIdx.y : blockIdx.x;
+    const unsigned by = SEG_MAJOR ? blockIdx.x : blockIdx.y;
+    const long long row_step = (long long)(SEG_MAJOR ? gridDim.x : gridDim.y) * RB;
+    const int m = bx * 64 + lane;
     const bool active = m < chunks_per_row;
     if (!STAGE && !active) return;
     const size_t row_bytes = (size_t)W * C;
     uint8_t *lds = lds_all + threadIdx.y * 64 * OUT;
-    const int seg_bytes = min(64, chunks_per_row - (int)blockIdx.x * 64) * OUT;
+    const int seg_bytes = min(64, chunks_per_row - (int)bx * 64) * OUT;
     // t is uniform across the wave
-    for (long long t = (long long)blockIdx.y * RB + threadIdx.y; t < rows;
-         t += (long long)gridDim.y * RB) {
+    for (long long t = (long long)by * RB + threadIdx.y; t < rows; t += row_step) {
         // source row t of the flattened N*H rows feeds output rows 2t, 2t + 1
-        uint8_t *d0 = dst + (size_t)(2 * t) * (2 * row_bytes) + (size_t)blockIdx.x * 64 * OUT;
+        uint8_t *d0 = dst + (size_t)(2 * t) * (2 * row_bytes) + (size_t)bx * 64 * OUT;
         if (active) {
             // the chunk starts at m * IN bytes into a row of W C bytes (a
             // multiple of 16): aligned to 16 bytes, or to IN when IN < 16
