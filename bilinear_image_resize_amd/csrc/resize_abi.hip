@@ -242,8 +242,8 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, long lo
 }
 
 template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false,
-          int B = kBorderClamp>
-bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+          int B = kBorderClamp, int PXO = 0>
+bool try_rowseg_px(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                 hipStream_t st, int &rc, const Affine &aff = Affine{},
                 const int32_t *rois = nullptr, int nn_map = kNearestHalfPixel)
 {
@@ -259,7 +259,8 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     // five-row bands, 161.4 with six); crops are sized against their own
     // regions, so only whole images count
     const bool enlarge = !ROI && (long long)dH * dW > (long long)H * W;
-    if (!plan_rowseg(SegShape<T, C>::PX, C * (int)sizeof(T), W, dW, rows, min_rows, enlarge, pl))
+    constexpr int PX = PXO ? PXO : SegShape<T, C>::PX;
+    if (!plan_rowseg(PX, C * (int)sizeof(T), W, dW, rows, min_rows, enlarge, pl))
         return false;
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8;
     // a slot then holds 64 lanes x that many chunks (the kernel writes its
@@ -272,7 +273,7 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const int slot_bytes = pl.seg_cap + (B == kBorderWrap ? 32 : 0);
     if (2 * slot_bytes > kSegLdsBudget) return false;
     auto go = [&](auto kernel) {
-        constexpr int nstage = seg_nhwc_stage_bytes<T, C, OUT>();
+        constexpr int nstage = seg_nhwc_stage_bytes<T, C, OUT, PX>();
         // at most 4 x (16 KiB of slots + 4 KiB of output staging) = 80 KiB,
         // within the 160 KiB one gfx950 workgroup may use
         static_assert(kSegWaves * (kSegLdsBudget + nstage) <= 160 * 1024, "LDS per workgroup");
@@ -291,10 +292,10 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     const bool stream = NEAREST ? H >= dH : H >= 2 * dH;
     auto pick = [&](auto nt) {
         constexpr bool NT = decltype(nt)::value;
-        if (per_lane <= 1) return go(rowseg<T, C, NEAREST, 1, NT, OUT, ROI, B>);
-        if (per_lane <= 2) return go(rowseg<T, C, NEAREST, 2, NT, OUT, ROI, B>);
-        if (per_lane <= 4) return go(rowseg<T, C, NEAREST, 4, NT, OUT, ROI, B>);
-        return go(rowseg<T, C, NEAREST, 8, NT, OUT, ROI, B>);
+        if (per_lane <= 1) return go(rowseg<T, C, NEAREST, 1, NT, OUT, ROI, B, PXO>);
+        if (per_lane <= 2) return go(rowseg<T, C, NEAREST, 2, NT, OUT, ROI, B, PXO>);
+        if (per_lane <= 4) return go(rowseg<T, C, NEAREST, 4, NT, OUT, ROI, B, PXO>);
+        return go(rowseg<T, C, NEAREST, 8, NT, OUT, ROI, B, PXO>);
     };
     if constexpr (!ROI && B == kBorderClamp) {
         if (stream) {
@@ -304,6 +305,60 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
     }
     rc = pick(std::false_type{});
     return true;
+}
+
+// Output pixels per lane of a one-channel uint8 row segment (a wave covers
+// 64 PX columns): the largest of 16 (nearest only), 8 and 4 whose segments
+// are at least 80% filled by the row, else the best-filled one.  More
+// pixels per lane spread each lane's set-up over more output, while lanes
+// past the row's end idle.  Measured (us, linear / nearest; PX 16, 8, 4):
+// 256 x 640x480 -> 224x224 57.7 / 25.7, 38.5 / 23.1, 33.1 / 21.1;
+// 4K -> 1440x2560 11.2 / 6.8, 9.7 / 7.2, 10.8 / 8.3; 32 x 720p -> 360x500
+// 19.1 / 9.8, 13.1 / 9.0, 16.7 / 11.5; 8K -> 1000x700 12.8 / 7.5,
+// 9.4 / 6.6, 7.9 / 6.2; 8 x 1080p -> 720p 16.7 / 9.3, 15.0 / 9.9,
+// 18.2 / 12.6 (the one miss: nearest takes 8 there).
+inline int seg_px_u8_c1(int dW, bool nearest)
+{
+    int best = 4;
+    long long best_num = 0, best_den = 1;   // best fill so far, as a fraction
+    for (int px = nearest ? 16 : 8; px >= 4; px /= 2) {
+        const long long cols = (long long)kSegLanes * px;
+        const long long span = ((dW + cols - 1) / cols) * cols;
+        if (5LL * dW >= 4LL * span) return px;   // fill >= 80%
+        if ((long long)dW * best_den > best_num * span) {
+            best = px;
+            best_num = dW;
+            best_den = span;
+        }
+    }
+    return best;
+}
+
+template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false,
+          int B = kBorderClamp>
+bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                hipStream_t st, int &rc, const Affine &aff = Affine{},
+                const int32_t *rois = nullptr, int nn_map = kNearestHalfPixel)
+{
+    if constexpr (sizeof(T) == 1 && C == 1) {
+        switch (seg_px_u8_c1(dW, NEAREST)) {
+        case 16:
+            if constexpr (NEAREST)
+                return try_rowseg_px<T, C, NEAREST, OUT, ROI, B, 16>(src, dst, batch, H, W, dH,
+                                                                     dW, st, rc, aff, rois, nn_map);
+            break;
+        case 8:
+            return try_rowseg_px<T, C, NEAREST, OUT, ROI, B, 8>(src, dst, batch, H, W, dH, dW, st,
+                                                                rc, aff, rois, nn_map);
+        default:
+            break;
+        }
+        return try_rowseg_px<T, C, NEAREST, OUT, ROI, B, 4>(src, dst, batch, H, W, dH, dW, st,
+                                                            rc, aff, rois, nn_map);
+    } else {
+        return try_rowseg_px<T, C, NEAREST, OUT, ROI, B>(src, dst, batch, H, W, dH, dW, st, rc,
+                                                         aff, rois, nn_map);
+    }
 }
 
 // Waves per workgroup of the exact 2x kernels (one source row or row gap

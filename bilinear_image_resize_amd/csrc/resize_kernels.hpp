@@ -988,6 +988,7 @@ __global__ __launch_bounds__(kBlock) void nearest_generic(
 // stays within its LDS budget; stronger downscales take the direct kernels.
 // --------------------------------------------------------------------------
 template <typename T, int C> struct SegShape;   // PX = output pixels per lane
+// one-channel uint8: the launcher picks 16, 8 or 4 per output width
 template <> struct SegShape<uint8_t, 1> { static constexpr int PX = 16; };
 template <> struct SegShape<uint8_t, 3> { static constexpr int PX = 4; };
 template <> struct SegShape<uint8_t, 4> { static constexpr int PX = 4; };
@@ -1232,11 +1233,11 @@ constexpr bool kSegStageFloatRgb = true;
 // floats per wave, after all waves' slots) and out as lane-contiguous
 // 16-byte non-temporal stores.  Compile-time: only this output stage has
 // the code and the LDS.
-template <typename T, int C, int OUT>
+template <typename T, int C, int OUT, int PX = SegShape<T, C>::PX>
 __host__ __device__ constexpr int seg_nhwc_stage_bytes()
 {
     return OUT == kOutNormNHWC || (kSegStageFloatRgb && OUT == kOutSame && sizeof(T) == 4 && C == 3)
-               ? kSegLanes * SegShape<T, C>::PX * C * 4
+               ? kSegLanes * PX * C * 4
                : 0;
 }
 __host__ __device__ inline bool seg_nhwc_staged(const void *dst, int dW, int C)
@@ -1245,7 +1246,7 @@ __host__ __device__ inline bool seg_nhwc_staged(const void *dst, int dW, int C)
 }
 
 template <typename T, int C, bool NEAREST, int KMAX, bool NT, int OUT = kOutSame, bool ROI = false,
-          int B = kBorderClamp>
+          int B = kBorderClamp, int PXO = 0>
 __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     const T *__restrict__ src, void *__restrict__ dst_v, int H, int W, int dH, int dW,
     long long rows_total, int rows_per_block, int seg_cap, long long src_elems, Affine aff,
@@ -1253,7 +1254,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
 {
     T *const dst = (T *)dst_v;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
-    constexpr int PX = SegShape<T, C>::PX;
+    constexpr int PX = PXO ? PXO : SegShape<T, C>::PX;   // PXO: the launcher's choice
     constexpr int PB = C * (int)sizeof(T);        // bytes per pixel
     static_assert(B == kBorderClamp || (!NEAREST && !ROI && OUT == kOutSame),
                   "mirror / wrap borders are for the plain linear resize");
@@ -1267,7 +1268,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     // wave index, made visibly uniform so that all per-row planning stays scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kSegLanes);
     uint8_t *const lds = lds_all + (size_t)wave * 2 * slot_bytes;   // this wave's two slots
-    constexpr int NSTAGE = seg_nhwc_stage_bytes<T, C, OUT>();
+    constexpr int NSTAGE = seg_nhwc_stage_bytes<T, C, OUT, PX>();
     [[maybe_unused]] const bool nstaged = NSTAGE > 0 && seg_nhwc_staged(dst_v, dW, C);
     [[maybe_unused]] uint8_t *const lds_n =
         lds_all + (size_t)kSegWaves * 2 * slot_bytes + (size_t)wave * NSTAGE;
