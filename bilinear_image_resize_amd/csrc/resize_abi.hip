@@ -334,6 +334,29 @@ inline int seg_px_u8_c1(int dW, bool nearest)
     return best;
 }
 
+// 8 output pixels per lane instead of 4 for uint8 RGB / RGBA and
+// one-channel float (plain output only): where the row fills its 512-column
+// segments (uint8 to 95%, float to 80%) and shrinks by at most 1.6 (linear)
+// or not at all (uint8 nearest), more pixels per lane spread each lane's
+// set-up.  Stronger shrinking stages more source per lane and halves the
+// waves, which costs more.  Measured (us, PX 4 -> 8): 4K -> 1440x2560 RGB
+// linear 13.7 -> 12.0, RGBA 15.1 -> 13.5 (nearest RGB 11.7 -> 11.0 but
+// RGBA 9.7 -> 10.3, so not taken); 1080p -> 2000x3000 RGB 17.3 -> 15.4 /
+// 13.1 -> 11.8, RGBA 18.8 -> 17.7 / 10.1 -> 9.6; one-channel float 4K ->
+// 1440x2560 linear 11.2 -> 10.0, 8 x 1080p -> 720p 18.6 -> 17.8 (nearest
+// slower: 9.6 -> 10.5).  Not taken where they lost: 32 x 720p -> 360x500
+// RGB (fills 98%, shrinks 2.56) 21.5 -> 23.5, 8 x 1080p -> 720p RGBA
+// (fills 83%) 24.1 -> 25.3.
+template <typename T, int C>
+bool seg_wide_px8(int W, int dW, bool nearest)
+{
+    const long long span = ((dW + 511) / 512) * 512;
+    const bool filled = sizeof(T) == 1 ? 20LL * dW >= 19LL * span : 5LL * dW >= 4LL * span;
+    if (!filled) return false;
+    if (nearest) return sizeof(T) == 1 && W <= dW;
+    return 5LL * W <= 8LL * dW;
+}
+
 template <typename T, int C, bool NEAREST, int OUT = kOutSame, bool ROI = false,
           int B = kBorderClamp>
 bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
@@ -356,6 +379,12 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
         return try_rowseg_px<T, C, NEAREST, OUT, ROI, B, 4>(src, dst, batch, H, W, dH, dW, st,
                                                             rc, aff, rois, nn_map);
     } else {
+        if constexpr (((sizeof(T) == 1 && C >= 3) || (sizeof(T) == 4 && C == 1)) &&
+                      OUT == kOutSame && !ROI && B == kBorderClamp) {
+            if (seg_wide_px8<T, C>(W, dW, NEAREST))
+                return try_rowseg_px<T, C, NEAREST, OUT, ROI, B, 8>(src, dst, batch, H, W, dH, dW,
+                                                                    st, rc, aff, rois, nn_map);
+        }
         return try_rowseg_px<T, C, NEAREST, OUT, ROI, B>(src, dst, batch, H, W, dH, dW, st, rc,
                                                          aff, rois, nn_map);
     }

@@ -201,6 +201,33 @@ def test_rowseg_rgb_enlargements(dtype, monkeypatch):
                           "rowseg rgb enlarge %s %s %s" % (dtype, mode, (N, H, W, dH, dW)))
 
 
+def test_rowseg_lane_widths(monkeypatch):
+    """The row-segment kernel's output pixels per lane follow the output
+    width: 16, 8 or 4 for one-channel uint8 (by how full the row leaves its
+    wave segments), 8 instead of 4 for wide uint8 RGB / RGBA and
+    one-channel float rows that shrink little or grow.  Each shape below
+    lands on one of those choices, with full, ragged and nearly full last
+    segments; linear and nearest."""
+    monkeypatch.setenv("MI_RESIZE_PATH", "rowseg")
+    r = np.random.default_rng(8181)
+    cases = [  # (dtype, C, N, H, W, dH, dW)
+        ("u8", 1, 2, 11, 640, 7, 224), ("u8", 1, 1, 9, 2100, 5, 700),
+        ("u8", 1, 1, 8, 3000, 6, 1900), ("u8", 1, 2, 9, 1920, 6, 1280),
+        ("u8", 1, 1, 7, 200, 5, 96), ("u8", 1, 1, 5, 1500, 9, 2047),
+        ("u8", 3, 1, 9, 3840, 6, 2560), ("u8", 3, 1, 6, 1920, 11, 3000),
+        ("u8", 3, 2, 7, 1500, 5, 1030), ("u8", 3, 1, 8, 3825, 5, 2550),
+        ("u8", 4, 1, 9, 3000, 6, 2048), ("u8", 4, 1, 5, 1500, 8, 2000),
+        ("f32", 1, 1, 9, 1920, 6, 1280), ("f32", 1, 1, 5, 2000, 9, 2560),
+        ("f32", 1, 2, 7, 1600, 5, 1021),
+    ]
+    for mode in ("linear", "nearest"):
+        for (dt, C, N, H, W, dH, dW) in cases:
+            say("case rowseg lanes %s %s %s" % (mode, dt, (C, N, H, W, dH, dW)))
+            s = random_image(r, (N, H, W, C), dt)
+            assert_parity(run_gpu(s, dH, dW, mode), run_oracle(s, dH, dW, mode),
+                          "rowseg lanes %s %s %s" % (mode, dt, (C, N, H, W, dH, dW)))
+
+
 @pytest.mark.parametrize("C", [3, 4])
 def test_direct_float_enlargements(C):
     """Float RGB / RGBA enlargements take the direct kernels: whole 16-byte
