@@ -456,7 +456,9 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // 8 x 1080p RGB 11.10 -> 10.89 us); there the segment-major order is slower
 // (4K RGBA 8.71 us), and so is a one-dimensional grid (4K RGB 6.82 us
 // without the renumbering, 6.54 with it).  Eight pixels per lane instead of
-// four (RGB, RGBA) measured slower on the 4K frames (RGB 6.52 -> 6.97 us).
+// four (RGB, RGBA) measured slower on the 4K frames (RGB 6.52 -> 6.97 us),
+// and so did fewer workgroups looping over 2 or 4 rows each (6.39 -> 6.75 /
+// 6.90 us): one row per wave keeps the most loads in flight.
 // --------------------------------------------------------------------------
 template <int C> struct HalfShape { static constexpr int PX = C == 1 ? 16 : 4; };
 

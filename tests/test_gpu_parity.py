@@ -694,6 +694,35 @@ def test_grey_4k_full_size():
 # batches beyond the 65535 grid extent: the exact 2x, exact 2:1, nearest and
 # direct kernels stride over images or rows past one grid's reach
 # --------------------------------------------------------------------------
+def _sampled_parity(s, dH, dW, mode, what, picks):
+    """Full-batch GPU run, compared with the oracle image by image on the
+    picked images (batches too large for the oracle as a whole)."""
+    got = run_gpu(s, dH, dW, mode)
+    for i in picks:
+        assert_parity(got[i:i + 1], run_oracle(s[i:i + 1], dH, dW, mode), "%s image %d" % (what, i))
+
+
+@pytest.mark.parametrize("case", ["wide", "tall"])
+def test_half_grid_row_loops(case):
+    """The exact 2:1 kernel past its grids' row reach.  wide: three
+    segments per row (520 RGB pixels: 256 + 256 + 8) take the row-major
+    grid with XCD-contiguous numbering, capped at 65535 rows, over 68000
+    output rows.  tall: one segment per row takes the segment-major grid,
+    rows along x capped at 2^24, over 2^24 + 1000 one-row images.
+    Sampled images cover the first and last rows, rows on both sides of
+    each cap and a spread between."""
+    r = np.random.default_rng(1313 + (case == "tall"))
+    if case == "wide":
+        N, H, W, C = 17000, 8, 1040, 3
+        picks = [0, 1, 16383, 16384, 16999] + [int(v) for v in r.integers(0, N, 20)]
+    else:
+        N, H, W, C = (1 << 24) + 1000, 2, 32, 1   # 16 output pixels: one segment
+        picks = [0, (1 << 24) - 1, 1 << 24, N - 1] + [int(v) for v in r.integers(0, N, 20)]
+    s = random_image(r, (N, H, W, C), "u8")
+    say("case half grid row loop %s %s" % (case, (N, H, W, C)))
+    _sampled_parity(s, H // 2, W // 2, "linear", "half row loop %s" % case, sorted(set(picks)))
+
+
 @pytest.mark.parametrize("case", ["up2", "half", "generic", "rowseg"])
 def test_batches_beyond_grid_extent(case, monkeypatch):
     r = np.random.default_rng(1212)
