@@ -1395,7 +1395,6 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         }
     };
     set_segment();
-    lane_table(crop, seg_sa);
     AxisStepper ys;
     auto row_init = [&](int d) {
         ys.init_biased(d, crop.h, dH, NEAREST ? nearest_bias(nn_map, crop.h, dH) : crop.h - dH);
@@ -1508,6 +1507,9 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         ha = halo_load(P.A, P.row_a);
         hb = halo_load(P.B, P.row_b);
     }
+    // the lanes' column table (fp64 per lane) is built while the band's
+    // first rows load: nothing before the first commit reads it
+    lane_table(crop, seg_sa);
 
     for (; g < g_end; ++g) {
         commit_segment<KMAX>(P.A, va, lo, hi);
