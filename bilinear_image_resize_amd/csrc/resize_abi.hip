@@ -172,10 +172,20 @@ constexpr int kSegLdsBudget = 16 * 1024;
 constexpr long long kSegTargetBands = 65536;
 constexpr long long kSegMinBandRows = 2;
 // Where each output pixel is a single byte (grey output, one-channel uint8),
-// a row moves little and the per-band set-up weighs more: three-row bands
-// (thumbnail batch to grey 48.6 -> 44.4 us, 2x one-channel enlargement on
-// this kernel 15.5 -> 13.5 us; wider outputs measured better or equal at two).
-constexpr long long kSegMinBandRowsNarrow = 3;
+// a row moves little and the per-band set-up weighs more, so bands are
+// longer - but only as long as enough of them remain to fill the chip.  By
+// row segments (output rows x wave segments per row): below 9000, two-row
+// bands; below 30000, three; else four.  Measured (us, one-channel linear;
+// bands of 2 / 3 / 4 rows): 4K -> 1000x1900 (4000 segments) 7.3 / 8.8 /
+// 8.6; 64 x 640x480 -> 112x112 (7168) 8.0 / 8.6 / 8.5; 32 x 720p ->
+// 360x500 (11520) 13.0 / 12.7 / 13.0; 8 x 1080p -> 720p (17280) 16.3 /
+// 14.8 / 14.9; 256 x 640x480 -> 224x224 (57344) 36.2 / 32.5 / 30.5.
+inline long long seg_min_rows_narrow(long long rows, int dW, int px)
+{
+    const long long cols = (long long)kSegLanes * px;
+    const long long segs = rows * ((dW + cols - 1) / cols);
+    return segs < 9000 ? 2 : (segs < 30000 ? 3 : 4);
+}
 // A crop-then-resize band first reads its image's region from device memory
 // before it can map a row, so its bands are made longer to amortise that
 // round trip (random crops of the thumbnail batch: 2 rows 44.9 us, 4 rows
@@ -252,14 +262,15 @@ bool try_rowseg_px(const void *src, void *dst, int batch, int H, int W, int dH, 
     // a crop is at most W wide, so the whole-image bound covers every crop
     constexpr int out_px_bytes =
         OUT == kOutGrey ? (int)sizeof(T) : (OUT == kOutSame ? C * (int)sizeof(T) : 4 * C);
+    constexpr int PX = PXO ? PXO : SegShape<T, C>::PX;
     const long long min_rows = ROI ? kSegMinBandRowsRoi
-                                   : (out_px_bytes == 1 ? kSegMinBandRowsNarrow : kSegMinBandRows);
+                               : (out_px_bytes == 1 ? seg_min_rows_narrow(rows, dW, PX)
+                                                    : kSegMinBandRows);
     // the output outweighs the source (pixel counts: rgbaf enlarges its
     // rows but halves its columns and is bandwidth-bound, 154.5 us with
     // five-row bands, 161.4 with six); crops are sized against their own
     // regions, so only whole images count
     const bool enlarge = !ROI && (long long)dH * dW > (long long)H * W;
-    constexpr int PX = PXO ? PXO : SegShape<T, C>::PX;
     if (!plan_rowseg(PX, C * (int)sizeof(T), W, dW, rows, min_rows, enlarge, pl))
         return false;
     // chunks of 16 bytes per lane per staged row, rounded up to 1, 2, 4 or 8;
