@@ -170,6 +170,12 @@ constexpr int kSegLdsBudget = 16 * 1024;
 // column table, in fp64) is paid once per band, so single-row bands cost
 // more than they gain.
 constexpr long long kSegTargetBands = 65536;
+// Multi-byte outputs keep two-row bands: three or four measured slower on
+// most shapes (64 x 640x480 -> 112x112 RGB 9.5 -> 10.2 / 10.6 us, float
+// 16 x 640x480 -> 224x224 RGBA 17.1 -> 18.6 / 18.5, thumbnail nearest 27.2
+// -> 28.4 / 28.7), faster on a few (8 x 1080p -> 720p RGB 23.1 -> 21.8 /
+// 21.6, thumbnail linear 47.1 -> 46.7 / 49.3), with no row-segment count
+// separating the two.
 constexpr long long kSegMinBandRows = 2;
 // Where each output pixel is a single byte (grey output, one-channel uint8),
 // a row moves little and the per-band set-up weighs more, so bands are
