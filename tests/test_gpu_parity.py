@@ -205,7 +205,9 @@ def test_rowseg_lane_widths(monkeypatch):
     """The row-segment kernel's output pixels per lane follow the output
     width: 16, 8 or 4 for one-channel uint8 (by how full the row leaves its
     wave segments), 8 instead of 4 for wide uint8 RGB / RGBA and
-    one-channel float rows that shrink little or grow.  Each shape below
+    one-channel float rows that shrink little or grow, and for float RGB
+    nearest rows that shrink by at most 2.1 (the last three float RGB cases:
+    8, 8 and, shrinking 2.7, 4 under nearest; 4 under linear).  Each shape below
     lands on one of those choices, with full, ragged and nearly full last
     segments; linear and nearest."""
     monkeypatch.setenv("MI_RESIZE_PATH", "rowseg")
@@ -219,6 +221,8 @@ def test_rowseg_lane_widths(monkeypatch):
         ("u8", 4, 1, 9, 3000, 6, 2048), ("u8", 4, 1, 5, 1500, 8, 2000),
         ("f32", 1, 1, 9, 1920, 6, 1280), ("f32", 1, 1, 5, 2000, 9, 2560),
         ("f32", 1, 2, 7, 1600, 5, 1021),
+        ("f32", 3, 1, 7, 3840, 5, 1900), ("f32", 3, 2, 6, 1500, 4, 1270),
+        ("f32", 3, 1, 5, 3000, 4, 1100),
     ]
     for mode in ("linear", "nearest"):
         for (dt, C, N, H, W, dH, dW) in cases:
