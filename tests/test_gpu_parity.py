@@ -218,6 +218,7 @@ def test_rowseg_lane_widths(monkeypatch):
         ("u8", 1, 1, 7, 200, 5, 96), ("u8", 1, 1, 5, 1500, 9, 2047),
         ("u8", 3, 1, 9, 3840, 6, 2560), ("u8", 3, 1, 6, 1920, 11, 3000),
         ("u8", 3, 2, 7, 1500, 5, 1030), ("u8", 3, 1, 8, 3825, 5, 2550),
+        ("u8", 3, 1, 6, 2560, 4, 2040), ("u8", 4, 1, 6, 2560, 4, 2040),
         ("u8", 4, 1, 9, 3000, 6, 2048), ("u8", 4, 1, 5, 1500, 8, 2000),
         ("f32", 1, 1, 9, 1920, 6, 1280), ("f32", 1, 1, 5, 2000, 9, 2560),
         ("f32", 1, 2, 7, 1600, 5, 1021),
