@@ -203,6 +203,10 @@ constexpr long long kSegMinBandRowsRoi = 4;
 // 9.8 -> 9.4; 1080p -> 1620x2880 RGB 16.3 -> 14.7, RGBA 17.4 -> 16.0;
 // 8x300x400 -> 1000x1200 RGB 29.3 -> 24.5; 2000^2 -> 3000^2 float 22.1 ->
 // 17.5; fewer bands than this left too few waves, more rows were slower).
+// Retested once wide enlargements took 8 pixels per lane (half the segments
+// per row): 2500 / 5000 / 10000 bands, 1080p -> 2000x3000 RGB 17.3 / 14.9 /
+// 15.0 us, 8 x 480x640 -> 720x1000 RGB 17.3 / 14.9 / 15.0, 4K grey ->
+// 3000x5000 19.6 / 19.6 / 21.4.
 constexpr long long kSegTargetBandsUp = 5000;
 constexpr long long kSegMinBandRowsUp = 3;
 constexpr long long kSegMaxBandRowsUp = 6;
