@@ -429,6 +429,10 @@ bool try_rowseg(const void *src, void *dst, int batch, int H, int W, int dH, int
 // RGBA -> 2x): linear 1 wave 4.13 / 9.65 / 8.53, 2 waves 3.67 / 8.92 / 8.52,
 // 4 waves 3.53 / 8.73 / 8.78; nearest 1 wave 3.14 / 6.90 / 7.47, 2 waves
 // 3.05 / 6.64 / 7.54, 4 waves 3.05 / 6.58 / 7.60.
+// Retested after the XCD-contiguous / segment-major grids and the
+// first-row prologue: linear 2 / 4 / 8 waves, 1080p -> 4K grey 3.70 / 3.60
+// / 3.88 us, RGB 6.53 / 6.03 / 6.78; nearest 1 / 2 / 4 waves, 4 x 720p grey
+// 4.20 / 3.65 / 3.65, 1080p -> 4K RGB 5.47 / 5.56 / 5.68.
 template <int C> constexpr int kUp2RowsLinear = C == 4 ? 2 : 4;
 template <int C> constexpr int kUp2RowsNearest = C == 4 ? 1 : 2;
 
