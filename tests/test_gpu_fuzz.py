@@ -3,7 +3,8 @@
 Each case draws an operation (linear, nearest under its three mappings,
 mirror / wrap borders, fused grey, fused normalisation, crop-then-resize), a
 kernel family (MI_RESIZE_PATH auto / rowseg / direct), a dtype, a shape
-(sizes 1-259, scale 0.08x-9x, some exact 2x and 2:1 cases) and sometimes a
+(sizes 1-259, scale 0.08x-9x, some exact 2x and 2:1 cases; or wide, short
+images up to 3199 wide) and sometimes a
 misaligned source, and compares the result with the oracle: uint8 and
 nearest bit-exact, float32 within 1e-5, normalised output within
 1e-5 * max(1, |v|).  Every case prints its name before its GPU work.
@@ -32,6 +33,16 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+def _shape_wide(r):
+    """Wide, short images (widths up to 3199, scale 0.3x-3x): rows of
+    several wave segments, where the row-segment kernel's pixels-per-lane
+    choice and its fill thresholds decide the launch."""
+    N = int(r.choice([1, 2, 3, 5]))
+    H, W = int(r.integers(1, 24)), int(r.integers(1, 3200))
+    sy, sx = np.exp(r.uniform(np.log(0.3), np.log(3.0), size=2))
+    return N, H, W, int(min(max(1, round(H * sy)), 40)), int(min(max(1, round(W * sx)), 3200))
+
+
 def _shape(r):
     N = int(r.choice([1, 2, 3, 5]))
     H, W = (int(v) for v in r.integers(1, 260, size=2))
@@ -43,9 +54,9 @@ def _shape(r):
     return N, H, W, dH, dW
 
 
-def _run(r, op, path, monkeypatch, i):
+def _run(r, op, path, monkeypatch, i, shape=_shape):
     monkeypatch.setenv("MI_RESIZE_PATH", path)
-    N, H, W, dH, dW = _shape(r)
+    N, H, W, dH, dW = shape(r)
     C = int(r.choice([3, 4])) if op == "grey" else int(r.choice([1, 3, 4]))
     dt = "u8" if op == "norm" else str(r.choice(["u8", "f32"]))
     s = random_image(r, (N, H, W, C), dt)
@@ -102,3 +113,10 @@ def test_random_mix(block, monkeypatch):
     for i in range(300):
         _run(r, OPS[i % len(OPS)], ["auto", "rowseg", "direct"][int(r.integers(0, 3))],
              monkeypatch, 300 * block + i)
+
+
+def test_random_mix_wide_rows(monkeypatch):
+    r = np.random.default_rng(31337)
+    for i in range(300):
+        _run(r, OPS[i % len(OPS)], ["auto", "rowseg", "direct"][int(r.integers(0, 3))],
+             monkeypatch, 900 + i, shape=_shape_wide)
