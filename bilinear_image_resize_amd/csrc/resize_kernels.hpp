@@ -458,7 +458,9 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // without the renumbering, 6.54 with it).  Eight pixels per lane instead of
 // four (RGB, RGBA) measured slower on the 4K frames (RGB 6.52 -> 6.97 us),
 // and so did fewer workgroups looping over 2 or 4 rows each (6.39 -> 6.75 /
-// 6.90 us): one row per wave keeps the most loads in flight.
+// 6.90 us): one row per wave keeps the most loads in flight.  Grey output
+// with 8 pixels per lane was slower too (4K -> 1080p grey 6.09-6.26 ->
+// 6.40-6.43 us), and would need widths that are multiples of 8 for RGBA.
 // --------------------------------------------------------------------------
 template <int C> struct HalfShape { static constexpr int PX = C == 1 ? 16 : 4; };
 
