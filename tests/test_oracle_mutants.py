@@ -27,6 +27,13 @@ MUTANTS = {
                   "+ U * (2048 - V) * s_ij1\n                            + (2048 - U) * V * s_i1j"),
     "truncate_result": ("(sum + ((int64_t)1 << 21)) >> 22", "sum >> 22"),
     "truncate_weight": ("floor_div(4096 * u_num + u_den, 2 * u_den)", "floor_div(4096 * u_num, 2 * u_den)"),
+    # weight ties (2048 u = k + 1/2) rounded half to even, or half down
+    "weight_round_half_even": ("return floor_div(4096 * u_num + u_den, 2 * u_den);",
+                               "int64_t q = floor_div(4096 * u_num + u_den, 2 * u_den);\n"
+                               "    if ((4096 * u_num + u_den) % (2 * u_den) == 0 && (q & 1))\n"
+                               "        q -= 1;\n    return q;"),
+    "weight_round_half_down": ("return floor_div(4096 * u_num + u_den, 2 * u_den);",
+                               "return floor_div(4096 * u_num + u_den - 1, 2 * u_den);"),
     "half_weight_v": ("int64_t V = quantise_11(v_num, v_den);", "int64_t V = quantise_11(v_num, v_den) / 2;"),
     "nearest_floor": ("floor_div(num + den / 2, den)", "floor_div(num, den)"),
     "f32_transposed": ("+ (1.0 - u) * v * s_ij1", "+ (1.0 - v) * u * s_ij1"),
@@ -55,7 +62,8 @@ def _pin_calls():
         argsets = [()]
         for mark in getattr(fn, "pytestmark", []):
             if mark.name == "parametrize":
-                argsets = [(v,) for v in mark.args[1]]
+                multi = "," in mark.args[0]
+                argsets = [tuple(v) if multi else (v,) for v in mark.args[1]]
         for args in argsets:
             yield name, fn, args
 

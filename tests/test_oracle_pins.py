@@ -11,6 +11,7 @@ GPUs" ("Naive resize with linear sampling": centre + 0.5 scaled into the
 input, linear filter), and hnwysp.cn news/129086 (s2.1 nearest, s2.2
 bilinear formula, s6.1 clamping, s6.2 fixed point).
 """
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -151,6 +152,96 @@ def test_ramp_u8_dyadic_scales(shape):
                 v = a + bx * sx + by * sy
                 assert out[dy, dx] == int(np.floor(v + Fraction(1, 2)))
     assert checked >= 2
+
+
+# --------------------------------------------------------------------------
+# uint8 weights at any scale.  The 11-bit weight of an axis is 2048 u rounded
+# half up (hnwysp.cn news/129086 s6.2, fixed point; the reading taken: one
+# rounding per axis, halves up), where u is the exact fractional part of the
+# half-pixel coordinate.  The four weights then sum to 2048^2 and blend a
+# linear ramp to the ramp's value at the *quantised* coordinate
+# i + U/2048, j + V/2048 (s2.2's four-term sum of a linear function), which
+# the final rounding takes half up.  Here U and V come from Fractions, never
+# from the oracle's integer code, so a wrong weight anywhere fails.
+# --------------------------------------------------------------------------
+def weight11_fraction(u):
+    """round-half-up(2048 u) for a Fraction u in [0, 1)."""
+    return math.floor(2048 * u + Fraction(1, 2))
+
+
+def quantised_coord(d, n_in, n_out):
+    """Clamped half-pixel coordinate with its fraction quantised to 11 bits."""
+    x = src_coord(d, n_in, n_out)
+    i = math.floor(x)
+    return i + Fraction(weight11_fraction(x - i), 2048)
+
+
+def ramp_expectation(a, bx, by, H, W, dH, dW):
+    ys = [quantised_coord(dy, H, dH) for dy in range(dH)]
+    xs = [quantised_coord(dx, W, dW) for dx in range(dW)]
+    return np.array([[math.floor(a + bx * x + by * y + Fraction(1, 2)) for x in xs]
+                     for y in ys], dtype=np.int64)
+
+
+def ramp_image(a, bx, by, H, W):
+    ys, xs = np.mgrid[0:H, 0:W]
+    vals = a + bx * xs + by * ys
+    assert vals.min() >= 0 and vals.max() <= 255
+    return vals.astype(np.uint8)[None, :, :, None]
+
+
+# Non-dyadic scales: the small image's scale 2/3 (64 -> 96), the thumbnail
+# batch's 15/7 and 20/7 (480 -> 224, 640 -> 224), and a few others.
+@pytest.mark.parametrize("shape,ramp", [
+    (((8, 12), (12, 18)), (5, 13, 11)),        # 1.5x both axes
+    (((6, 10), (9, 15)), (200, -9, -17)),
+    (((15, 20), (7, 7)), (3, 7, 8)),           # 480/224 and 640/224 ratios
+    (((30, 40), (14, 14)), (250, -3, -4)),
+    (((7, 5), (11, 13)), (1, 31, 19)),         # 7/11, 5/13
+    (((9, 4), (5, 7)), (17, 29, 13)),          # 9/5 down, 4/7 up
+])
+def test_ramp_u8_quantised_any_scale(shape, ramp):
+    (H, W), (dH, dW) = shape
+    a, bx, by = ramp
+    out = oracle.resize_linear(ramp_image(a, bx, by, H, W), dH, dW)[0, :, :, 0]
+    assert np.array_equal(out.astype(np.int64), ramp_expectation(a, bx, by, H, W, dH, dW))
+
+
+@pytest.mark.parametrize("axis", ["x", "y"])
+def test_weight_ties_round_half_up(axis):
+    """An odd source length resized to 2048 samples puts 2048 u on k + 1/2 at
+    every interior sample (u = r / 4096 with r odd), the only way a weight tie
+    arises; 6 -> 4096 does it too (2048 u = r / 4 with r = 2 mod 4).  The
+    ramp pins which way those ties go: half up."""
+    for n_in, n_out, a, b in ((3, 2048, 20, 101), (5, 2048, 2, 59), (6, 4096, 3, 48)):
+        ties = sum((2048 * (src_coord(d, n_in, n_out) - math.floor(src_coord(d, n_in, n_out)))).denominator == 2
+                   for d in range(n_out))
+        assert ties > n_out // 2
+        if axis == "x":
+            H, W, dH, dW, bx, by = 2, n_in, 3, n_out, b, 7
+        else:
+            H, W, dH, dW, bx, by = n_in, 2, n_out, 3, 7, b
+        out = oracle.resize_linear(ramp_image(a, bx, by, H, W), dH, dW)[0, :, :, 0]
+        assert np.array_equal(out.astype(np.int64), ramp_expectation(a, bx, by, H, W, dH, dW))
+
+
+def test_four_by_four_tables_by_hand():
+    """S = 16 (4y + x).  The tables below were worked by hand from the
+    definition (the pages print no worked example): 4 -> 3 puts the centres
+    at 1/6, 3/2, 17/6, so the 11-bit weights are 341, 1024, 1707 (341.33 and
+    1706.67 rounded), and an output is 16 (4 y_q + x_q) rounded half up at
+    the quantised coordinates, e.g. 80 * 341 / 2048 = 13.32 -> 13 at (0, 0).
+    4 -> 8 puts the centres at d/2 - 1/4, clamped at 0 and 3."""
+    S = (16 * (4 * np.arange(4)[:, None] + np.arange(4)[None, :])).astype(np.uint8)
+    assert [weight11_fraction(src_coord(d, 4, 3) % 1) for d in range(3)] == [341, 1024, 1707]
+    out3 = oracle.resize_linear(S, 3, 3)[0, :, :, 0]
+    assert out3.tolist() == [[13, 35, 56], [99, 120, 141], [184, 205, 227]]
+    out8 = oracle.resize_linear(S, 8, 8)[0, :, :, 0]
+    assert out8[0].tolist() == [0, 4, 12, 20, 28, 36, 44, 48]
+    assert out8[7].tolist() == [192, 196, 204, 212, 220, 228, 236, 240]
+    assert out8[:, 0].tolist() == [0, 16, 48, 80, 112, 144, 176, 192]
+    assert np.array_equal(out3.astype(np.int64), ramp_expectation(0, 16, 64, 4, 4, 3, 3))
+    assert np.array_equal(out8.astype(np.int64), ramp_expectation(0, 16, 64, 4, 4, 8, 8))
 
 
 # --------------------------------------------------------------------------
