@@ -20,7 +20,10 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
-    # packed fp32 instructions are kept out of the generated code
+    # No packed fp32 instructions (v_pk_add/mul/fma_f32) in the gfx950 code:
+    # the device pass honours this feature.  The host (x86) pass does not
+    # know it and prints that it ignores it; that warning is harmless.
+    # tests/test_code_object.py checks the built code object for them.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,

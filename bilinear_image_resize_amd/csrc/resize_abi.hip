@@ -42,9 +42,11 @@ Path path_override()
     return Path::Auto;
 }
 
-// dC: channels of dst (C unless the output stage changes them)
+// dC: channels of dst (C unless the output stage changes them); dst_es:
+// bytes per dst element (that of the dtype unless the output stage changes
+// the element type, as the normalising stage does)
 int check_args(const void *src, const void *dst, int batch, int H, int W, int C, int dtype,
-               int dH, int dW, int dC = 0)
+               int dH, int dW, int dC = 0, size_t dst_es = 0)
 {
     if (dC == 0) dC = C;
     if (!src || !dst) return MI_RESIZE_ERR_NULL;
@@ -55,11 +57,13 @@ int check_args(const void *src, const void *dst, int batch, int H, int W, int C,
     if ((long long)batch * dH * dW > kMaxOutPixels) return MI_RESIZE_ERR_SHAPE;
     if ((long long)batch * H * W > kMaxOutPixels) return MI_RESIZE_ERR_SHAPE;
     const size_t es = dtype == MI_RESIZE_U8 ? 1 : 4;
+    if (dst_es == 0) dst_es = es;
     const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
     const uintptr_t s1 = s0 + (size_t)batch * H * W * C * es;
-    const uintptr_t d1 = d0 + (size_t)batch * dH * dW * dC * es;
+    const uintptr_t d1 = d0 + (size_t)batch * dH * dW * dC * dst_es;
     if (s0 < d1 && d0 < s1) return MI_RESIZE_ERR_OVERLAP;
-    if (es == 4 && (!aligned(src, 4) || !aligned(dst, 4))) return MI_RESIZE_ERR_ALIGN;
+    if ((es == 4 && !aligned(src, 4)) || (dst_es == 4 && !aligned(dst, 4)))
+        return MI_RESIZE_ERR_ALIGN;
     return MI_RESIZE_OK;
 }
 
@@ -721,11 +725,10 @@ int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W
                             int dst_H, int dst_W, float alpha, const float *mean,
                             const float *std_dev, int layout, void *stream)
 {
-    if (!src || !dst) return MI_RESIZE_ERR_NULL;
-    if (C != 1 && C != 3 && C != 4) return MI_RESIZE_ERR_CHANNELS;
-    if (batch < 1 || H < 1 || W < 1 || dst_H < 1 || dst_W < 1 || H > kMaxDim || W > kMaxDim ||
-        dst_H > kMaxDim || dst_W > kMaxDim || (long long)batch * dst_H * dst_W > kMaxOutPixels)
-        return MI_RESIZE_ERR_SHAPE;
+    // uint8 source, float32 destination of C channels
+    const int rc = check_args(src, dst, batch, H, W, C, MI_RESIZE_U8, dst_H, dst_W, C,
+                              sizeof(float));
+    if (rc != MI_RESIZE_OK) return rc;
     if (!mean || !std_dev || (layout != 0 && layout != 1) || !isfinite(alpha))
         return MI_RESIZE_ERR_PARAM;
     Affine aff{};
@@ -735,11 +738,6 @@ int resize_linear_normalize(const void *src, float *dst, int batch, int H, int W
         aff.scale[c] = (float)((double)alpha / sd);
         aff.bias[c] = (float)(-mu / sd);
     }
-    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
-    const uintptr_t s1 = s0 + (size_t)batch * H * W * C;
-    const uintptr_t d1 = d0 + (size_t)batch * dst_H * dst_W * C * sizeof(float);
-    if (s0 < d1 && d0 < s1) return MI_RESIZE_ERR_OVERLAP;
-    if (!aligned(dst, 4)) return MI_RESIZE_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     if (layout == 0) {
         switch (C) {

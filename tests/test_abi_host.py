@@ -112,6 +112,16 @@ def test_normalize_validation():
     assert norm(alpha=float("nan")) == 8
     assert norm(dst=FAKE_DST + 2) == 7
     assert norm(dst=FAKE_SRC + 4) == 5
+    # the limits every entry point shares: dimensions, and at most 2^40
+    # source or destination pixels
+    assert norm(H=65536) == 2
+    assert norm(dW=70000) == 2
+    assert lib.resize_linear_normalize(FAKE_SRC, FAKE_DST, 1 << 30, 40000, 40000, 3, 1, 1,
+                                       1.0, mean, std, 1, None) == 2
+    assert lib.resize_linear_normalize(FAKE_SRC, FAKE_DST, 1 << 30, 4, 4, 3, 65535, 65535,
+                                       1.0, mean, std, 1, None) == 2
+    # shape errors come before parameter errors, as in the other entry points
+    assert norm(H=0, m=None) == 2
 
 
 def test_roi_validation():
