@@ -144,14 +144,18 @@ int launch_half_u8(const void *src, void *dst, int batch, int dH, int dW, hipStr
     if (segs <= 2) {
         const dim3 grid((unsigned)(rows < kMaxGridX ? rows : kMaxGridX), (unsigned)segs);
         return launch(linear_half_u8<C, GREY, true>, grid, dim3(kHalfLanes), 0, st,
-                      (const uint8_t *)src, (uint8_t *)dst, dW, rows, DivBy{});
+                      (const uint8_t *)src, (uint8_t *)dst, dW, rows, DivBy{}, (int)segs,
+                      rows);
     }
-    // workgroup numbers stay below 2^31 for the kernel's divide by segs
-    long long gy = rows < kMaxGridY ? rows : kMaxGridY;
-    if (segs * gy > kMaxGroups) gy = kMaxGroups / segs;
-    return launch(linear_half_u8<C, GREY, false>, dim3((unsigned)segs, (unsigned)gy),
-                  dim3(kHalfLanes), 0, st, (const uint8_t *)src, (uint8_t *)dst, dW, rows,
-                  make_div_by((unsigned)segs));
+    // a pass covers at most 65535 rows (the row loop is then exercised by
+    // batches of realistic size) and its items stay below 2^31 for the
+    // kernel's divide by segs
+    long long pass = rows < kMaxGridY ? rows : kMaxGridY;
+    if (segs * pass > kMaxGroups) pass = kMaxGroups / segs;
+    const long long wgs = (segs * pass + kHalfWaves - 1) / kHalfWaves;
+    return launch(linear_half_u8<C, GREY, false>, dim3((unsigned)wgs),
+                  dim3(kHalfLanes * kHalfWaves), 0, st, (const uint8_t *)src, (uint8_t *)dst,
+                  dW, rows, make_div_by((unsigned)segs), (int)segs, pass);
 }
 
 // Exact 2:1 uint8 downscale whose rows split into whole 16-byte chunks and

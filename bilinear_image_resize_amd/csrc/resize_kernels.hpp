@@ -432,8 +432,8 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // general formula reduces, bit for bit, to the rounded 2x2 mean
 // (a + b + c + d + 2) >> 2.  No tap is ever clamped.
 //
-// A workgroup is one wave and owns a segment of 64 * PX output pixels of one
-// output row (PX = 16 for C = 1, 4 for C = 3 and 4).  Each source row of the
+// A wave owns a segment of 64 * PX output pixels of one output row
+// (PX = 16 for C = 1, 4 for C = 3 and 4).  Each source row of the
 // segment (2 PX C bytes per lane) is read with 16-byte non-temporal loads at
 // lane-consecutive addresses - every load instruction covers whole cache
 // lines, which is what lets the streaming hint help - and staged in LDS; each
@@ -451,11 +451,11 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 // slower than the same workgroups laid along x (64 x 224x224 RGB: 5.28 ->
 // 4.08 us; 16 x 640x480 RGB: 5.82 -> 4.89 us, where the full first
 // segments of all rows also go out before the short second ones).  Wider
-// rows keep x = segment, y = output rows (stride gridDim.y) with the XCD
+// rows number their (row, segment) items row-major with the XCD
 // renumbering below (4K RGB 6.50 -> 6.40 us, 4K RGBA 8.38 -> 8.21 us,
-// 8 x 1080p RGB 11.10 -> 10.89 us); there the segment-major order is slower
-// (4K RGBA 8.71 us), and so is a one-dimensional grid (4K RGB 6.82 us
-// without the renumbering, 6.54 with it).  Eight pixels per lane instead of
+// 8 x 1080p RGB 11.10 -> 10.89 us, all on a 2-D grid of one-wave
+// workgroups, since replaced by the 1-D grid of two-wave workgroups); the
+// segment-major order is slower there (4K RGBA 8.71 us).  Eight pixels per lane instead of
 // four (RGB, RGBA) measured slower on the 4K frames (RGB 6.52 -> 6.97 us),
 // and so did fewer workgroups looping over 2 or 4 rows each (6.39 -> 6.75 /
 // 6.90 us): one row per wave keeps the most loads in flight.  Grey output
@@ -465,6 +465,16 @@ __global__ __launch_bounds__(kBlock) void linear_generic(
 template <int C> struct HalfShape { static constexpr int PX = C == 1 ? 16 : 4; };
 
 constexpr int kHalfLanes = 64;
+// Waves per workgroup of the row-major grid, each with its own segment.
+// Workgroups of one wave dispatch slowly: an empty launch of 8640 of them
+// costs 2.9 us back to back (4.6 us on the earlier 8 x 1080 2-D grid),
+// against 2.0 us for 4320 two-wave and 1.54 us for 2160 four-wave
+// workgroups.  A single 4K RGB launch does not see it (its dispatch
+// overlaps the memory phase: 6.43 us with one or two waves, 6.52 four,
+// 6.61 eight), but frames pipelined over three streams do, where the
+// dispatcher serves several grids at once: 5.41 us per frame with one
+// wave, 5.06-5.12 with two, 5.05-5.08 with four.
+constexpr int kHalfWaves = 2;
 
 
 __device__ __forceinline__ uint4 load_stream(const uint8_t *p)
@@ -504,10 +514,17 @@ __device__ __forceinline__ void store_staged(const uint8_t *lds, uint8_t *out, i
 // 6.85 us, the non-temporal hint on the 12-byte stores 6.54 -> 6.74 us
 // (though 5% faster on a 16 x 480x640 batch); non-temporal 16-byte stores
 // for grey 4K -> 1080p 4.01 -> 3.88 us.
+//
+// Segment-major workgroups are one wave; row-major ones kHalfWaves waves,
+// each wave with its own segment and LDS slot (no workgroup barrier).
+// Row-major: a 1-D grid over the (row, segment) items of a pass of
+// `pass_rows` output rows, wave w of workgroup b taking item
+// kHalfWaves b' + w, where b' numbers the workgroups XCD-contiguously; a
+// wave then steps by pass_rows rows while rows remain.
 template <int C, bool GREY, bool SEG_MAJOR>
-__global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
+__global__ __launch_bounds__(kHalfLanes * kHalfWaves) void linear_half_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int dW, long long rows,
-    DivBy by_segs)
+    DivBy by_segs, int segs, long long pass_rows)
 {
     static_assert(!GREY || C >= 3, "grey needs RGB(A)");
     constexpr int PX = HalfShape<C>::PX;
@@ -517,9 +534,12 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
     constexpr int LB = 2 * PX * C;                // source bytes per lane per row
     constexpr int OC = GREY ? 1 : C;              // output channels
     constexpr int OB = PX * OC;                   // output bytes per lane
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SRC_B];
+    constexpr int WAVES = SEG_MAJOR ? 1 : kHalfWaves;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[WAVES][2 * SRC_B];
 
-    const int lane = threadIdx.x;
+    const int lane = (int)threadIdx.x & (kHalfLanes - 1);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kHalfLanes);
+    uint8_t *const lds = lds_all[wave];
     int seg;
     long long g, g_step;
     if constexpr (SEG_MAJOR) {
@@ -527,13 +547,13 @@ __global__ __launch_bounds__(kHalfLanes) void linear_half_u8(
         g = blockIdx.x;
         g_step = gridDim.x;
     } else {
-        // each XCD takes a contiguous run of (row, segment) pairs
-        const unsigned gx = gridDim.x;
-        const unsigned wid = xcd_contiguous(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
-        const unsigned row = div_by(wid, by_segs);
-        seg = (int)(wid - row * gx);
+        // each XCD takes a contiguous run of (row, segment) items
+        const unsigned item = xcd_contiguous(blockIdx.x, gridDim.x) * WAVES + wave;
+        if (item >= (unsigned long long)pass_rows * segs) return;   // the last workgroup's spare wave
+        const unsigned row = div_by(item, by_segs);
+        seg = (int)(item - row * (unsigned)segs);
         g = row;
-        g_step = gridDim.y;
+        g_step = pass_rows;
     }
     const int seg_px = min(SEG, dW - seg * SEG);
     const int n16 = seg_px * 2 * C / 16;          // whole: dW meets the divisibility rule

@@ -302,6 +302,38 @@ def test_edge_shapes(dtype, mode, path, monkeypatch):
                       "edge %s" % ((N, H, W, C, dH, dW),))
 
 
+# --------------------------------------------------------------------------
+# 11-bit weight ties: an odd source length resized to a multiple of 2048
+# (or an even one with the right residue, 6 -> 4096) puts 2048 u exactly on
+# k + 1/2, which the resize rounds half up.  Every kernel family that takes
+# general scales must round those the same way as the oracle.
+# --------------------------------------------------------------------------
+TIE_SHAPES = [
+    (1, 3, 5, 2048, 2048),       # ties on both axes at almost every sample
+    (1, 2, 6, 4, 4096),          # 6 -> 4096: ties along x at every interior sample
+    (3, 7, 2049, 6, 2048),       # ties along x only, a slight downscale
+    (1, 2047, 9, 2048, 16),      # ties along y only
+]
+
+
+@pytest.mark.parametrize("C", [1, 3, 4])
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_weight_tie_shapes(dtype, C, monkeypatch):
+    r = np.random.default_rng(4242 + C)
+    shapes = TIE_SHAPES + ([(1, 1081, 1921, 2048, 2048)] if (dtype, C) == ("u8", 3) else [])
+    for (N, H, W, dH, dW) in shapes:
+        s = random_image(r, (N, H, W, C), dtype)
+        want = run_oracle(s, dH, dW)
+        for path in ["auto"] + PATHS:
+            if path == "auto":
+                monkeypatch.delenv("MI_RESIZE_PATH", raising=False)
+            else:
+                monkeypatch.setenv("MI_RESIZE_PATH", path)
+            say("case tie %s C=%d %s %s" % (dtype, C, path, (N, H, W, dH, dW)))
+            assert_parity(run_gpu(s, dH, dW), want,
+                          "tie %s C=%d %s %s" % (dtype, C, path, (N, H, W, dH, dW)))
+
+
 def test_golden_hand_cases():
     import json
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
