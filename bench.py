@@ -8,12 +8,25 @@ resident in HBM; the step rotates over enough (src, dst) buffer pairs that
 their total exceeds twice the 256 MB Infinity Cache, so each step reads its
 source from HBM, not from cache.
 
-Prints ONE JSON line with: Gpix/s (dst pixels per second, whole job), the
-kernel's HBM roofline (algorithmic bytes = src read once + dst written once,
-over the kernel's average duration measured with HIP events on the launch
-stream), and the CPU oracle timed on the host cores as a reported baseline.
+Prints ONE JSON line with: Gpix/s (dst pixels per second over the K timed
+steps), the kernel's HBM roofline (algorithmic bytes = src read once + dst
+written once, over the kernel's average duration), and the CPU oracle timed
+on the host cores as a reported baseline.
+
+Timing protocol of the headline: a bounded spin kernel (torch.cuda._sleep)
+holds the launch stream while the host enqueues the W warm-up steps and the K
+timed steps behind it, and a HIP event pair on that stream around the K
+timed steps gives their GPU time; synchronisation brackets the region.  The
+steps then run back to back as in a pipeline, starting in its steady state,
+and neither the host's call rate nor its synchronisation latency enters
+`value`.  The wall clock of the synchronised region (hold, warm-up and
+synchronisation included) is reported beside it.
+`sustained` (informational) times frames issued round-robin over several
+HIP streams the same way.
 
     python bench.py [--steps K] [--warmup W] [--workload 4k] [--no-cpu]
+    python bench.py --ceiling        (launch and bandwidth ceilings)
+    python bench.py --suite          (every workload, cold and warm, + oracle)
 """
 from __future__ import annotations
 
@@ -32,19 +45,32 @@ HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
 INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
-# dispatch), each scaled by the factor the same counter reads for the plain
-# 16-byte copy of 32 MiB (`bench.py --copy-calibration 33554432`: FETCH_SIZE
-# 16390.74 KiB -> x 1.9992, WRITE_SIZE 32798.97 KiB -> x 0.9991).  Valid only
-# for the kernel named; profiles/linear_half_u8_4k_rgb_pmc_traffic.md holds
-# the runs.  Workloads without an entry report null.
+# dispatch), each scaled by the factor the same counter reads for a copy of
+# known size (`bench.py --copy-calibration 33554432`).  Keys: (workload,
+# mode).  Each entry names the profile that holds its runs and the hash of
+# the kernel and launch sources it was taken on; bench.py reports null
+# traffic when they no longer hash to that value (the kernel changed since).
 MEASURED_TRAFFIC = {
-    ("4k", "linear"): {"kernel": "linear_half_u8<3, false, false>", "fetch_kib": 12175.86, "write_kib": 6075.0,
-                       "fetch_scale": 1.9992, "write_scale": 0.9991},
+    ("4k", "linear"): {"kernel": "linear_half_u8<3, false, false>",
+                       "profile": "profiles/linear_half_u8_4k_rgb_pmc_traffic.md",
+                       "kernel_source_sha256_16": "716059118abe56e4",
+                       "fetch_kib": 12176.86, "write_kib": 6075.0,
+                       "fetch_scale": 1.99833, "write_scale": 0.99911},
 }
 
 
+def kernel_source_hash():
+    """Hash of the kernel and launch sources (both decide what a launch does)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("resize_kernels.hpp", "resize_abi.hip"):
+        with open(os.path.join(ROOT, "bilinear_image_resize_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def traffic_bytes(entry):
-    if not entry:
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return round((entry["fetch_kib"] * entry["fetch_scale"] + entry["write_kib"] * entry["write_scale"]) * 1024)
 
@@ -75,8 +101,20 @@ def parse():
                    help="skip the per-launch event timing with trimming")
     p.add_argument("--no-copy", action="store_true",
                    help="skip the copy-kernel ceiling at the same bytes per launch")
-    p.add_argument("--no-pipelined", action="store_true",
-                   help="skip the extra two-stream pipelined measurement")
+    p.add_argument("--no-pipelined", "--no-sustained", dest="no_pipelined", action="store_true",
+                   help="skip the informational multi-stream (sustained) measurement")
+    p.add_argument("--no-warm", action="store_true",
+                   help="skip the informational warm-cache figure")
+    p.add_argument("--streams", type=int, default=3,
+                   help="HIP streams of the sustained measurement (default 3)")
+    p.add_argument("--ceiling", action="store_true",
+                   help="instead of resizing, run the launch / bandwidth ceiling program")
+    p.add_argument("--suite", action="store_true",
+                   help="instead of one workload, measure every workload cold and warm and "
+                        "time the oracle on each (single thread and all host cores)")
+    p.add_argument("--copy-kind", default="library", choices=["library", "torch"],
+                   help="--copy-calibration kernel: the library's 16-byte copy (non-temporal "
+                        "loads and stores) or torch's tensor copy (plain loads and stores)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="instead of resizing, time the plain 16-byte copy kernel on BYTES "
                         "bytes (cold rotation); used to scale HBM traffic counters")
@@ -98,20 +136,27 @@ def copy_calibration(args):
     lib = R._load()
     sh = torch.cuda.current_stream(dev).cuda_stream
     ptrs = [(a.data_ptr(), b.data_ptr()) for a, b in bufs]
+    def one(i):
+        if args.copy_kind == "torch":
+            bufs[i % pairs][1].copy_(bufs[i % pairs][0])
+            return
+        rc = lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+        if rc:
+            raise R.ResizeError(rc, "resize_copy_bytes")
+
     for i in range(args.warmup):
-        lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+        one(i)
     torch.cuda.synchronize(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
-        rc = lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
-        if rc:
-            raise R.ResizeError(rc, "resize_copy_bytes")
+        one(i)
     e1.record()
     torch.cuda.synchronize(dev)
     us = e0.elapsed_time(e1) * 1e3 / args.steps
-    print(json.dumps({"copy_bytes": n, "pairs": pairs, "kernel_us": round(us, 3),
+    print(json.dumps({"copy_bytes": n, "copy_kind": args.copy_kind, "pairs": pairs,
+                      "kernel_us": round(us, 3),
                       "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
@@ -136,10 +181,73 @@ def device_hbm_peak(dev_index=0):
             "GBps_at_4_per_clock": round(4 * clk.value * 1e3 * bus.value / 8 / 1e9, 1)}
 
 
-def copy_same_bytes(total_bytes, steps, lib, dev, sh):
+class StreamHold:
+    """Holds a stream with torch.cuda._sleep, a bounded spin kernel, while
+    the host enqueues a run of launches behind it: the HIP events around the
+    run then time launches that follow each other back to back on the GPU,
+    not the host's call rate.  The spin is calibrated once (clock cycles per
+    microsecond) with events."""
+
+    def __init__(self, dev, stream):
+        import torch
+        self.torch = torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(1000)
+            cycles = 2_000_000
+            e0.record(stream)
+            torch.cuda._sleep(cycles)
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        self.cycles_per_us = cycles / max(1e-3, e0.elapsed_time(e1) * 1e3)
+
+    def __call__(self, stream, us):
+        with self.torch.cuda.stream(stream):
+            self.torch.cuda._sleep(int(us * self.cycles_per_us))
+
+
+def timed_run(launch, n, streams, hold, enqueue_us, pre=None):
+    """GPU time per launch (ms) of n launches, launch(i, stream_handle) for
+    i in [0, n) on streams[i % S], held until all are enqueued, timed by a
+    HIP event pair on streams[0] joined with every other stream.  `pre`, if
+    given, is (launch function, count): untimed launches queued behind the
+    hold directly ahead of the timed ones, on streams[0], so that the timed
+    launches start in the steady state of a running queue.  Returns (ms per
+    launch, host enqueue seconds, whether the hold outlasted the enqueue)."""
+    import torch
+    main = streams[0]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n_pre = pre[1] if pre else 0
+    # about 1.5x the host's enqueue time, capped at one second (a slow host,
+    # e.g. under a tracing profiler, then shows as hold_covered_enqueue false)
+    hold_us = min(1.5 * (n + n_pre) * enqueue_us + 100.0, 1e6)
+    handles = [st.cuda_stream for st in streams]
+    t0 = time.perf_counter()
+    hold(main, hold_us)
+    for i in range(n_pre):
+        pre[0](i, handles[0])
+    e0.record(main)
+    for st in streams[1:]:
+        st.wait_event(e0)
+    for i in range(n):
+        launch(i, handles[i % len(handles)])
+    for st in streams[1:]:
+        ev = torch.cuda.Event()
+        ev.record(st)
+        main.wait_event(ev)
+    e1.record(main)
+    t_enq = time.perf_counter() - t0
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n, t_enq, t_enq * 1e6 < hold_us
+
+
+def copy_same_bytes(total_bytes, steps, lib, dev, stream, hold, enqueue_us):
     """A plain 16-byte copy kernel moving the same bytes per launch as one
     resize (total_bytes / 2 read + total_bytes / 2 written), over rotating
-    buffers that defeat the Infinity Cache, timed like the resize."""
+    buffers that defeat the Infinity Cache, timed like the resize (held
+    stream, HIP events)."""
     import torch
 
     n = (total_bytes // 2 + 15) // 16 * 16
@@ -147,20 +255,18 @@ def copy_same_bytes(total_bytes, steps, lib, dev, sh):
     bufs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(k & 255),
              torch.empty(n, dtype=torch.uint8, device=dev)) for k in range(pairs)]
     ptrs = [(a.data_ptr(), b.data_ptr()) for a, b in bufs]
+    bad = [0]
+
+    def launch(i, sh):
+        bad[0] |= lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+
     for i in range(2 * pairs):
-        lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
+        launch(i, stream.cuda_stream)
     torch.cuda.synchronize(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    bad = 0
-    for i in range(steps):
-        bad |= lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
-    e1.record()
-    torch.cuda.synchronize(dev)
-    if bad:
-        raise RuntimeError("resize_copy_bytes failed (%d)" % bad)
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    ms, _, _ = timed_run(launch, steps, [stream], hold, enqueue_us)
+    if bad[0]:
+        raise RuntimeError("resize_copy_bytes failed (%d)" % bad[0])
+    us = ms * 1e3
     del bufs
     return {"bytes_moved": 2 * n, "kernel_us": round(us, 3), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}
 
@@ -236,6 +342,115 @@ def cpu_single_thread(w, src_np, mode, budget_s):
             "sample": "%d whole %s frame(s), %.1f s, %.2f ms per frame" % (reps, w.name, el, per * 1e3)}
 
 
+def ceiling():
+    """Runs the ceiling program (copy throughput against size, empty-grid
+    launch costs, a read-only stream, the 4K frame on 1-4 streams, a
+    per-wave trace of a stand-in for the 2:1 kernel) and passes its JSON
+    lines through."""
+    import subprocess
+    exe = os.path.join(ROOT, "bilinear_image_resize_amd", "mi_resize_ceiling")
+    if not os.path.exists(exe):
+        sys.exit("the ceiling program is not built: run __graft_entry__.build() first")
+    sys.exit(subprocess.call([exe]))
+
+
+def oracle_rate(w, src_np, mode, threads, budget_s):
+    """Oracle Gpix/s on `threads` host threads over consecutive bands of
+    output rows (wrapping around the batch), for about budget_s seconds."""
+    import oracle
+
+    fn = oracle.resize_linear if mode == "linear" else oracle.resize_nearest
+    fn(src_np[:1], 1, 1)
+    rows_total = w.batch * w.dH
+    band = max(threads, min(rows_total, max(1, 200000 // w.dW)))
+    done, r0 = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        r1 = min(rows_total, r0 + band)
+        bounds = [r0 + (r1 - r0) * k // threads for k in range(threads + 1)]
+        ts = [threading.Thread(target=fn, args=(src_np, w.dH, w.dW),
+                               kwargs={"rows": (bounds[k], bounds[k + 1])})
+              for k in range(threads) if bounds[k + 1] > bounds[k]]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        done += r1 - r0
+        r0 = 0 if r1 == rows_total else r1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"Gpix_s": round(done * w.dW / el / 1e9, 5), "threads": threads,
+            "sample": "%d output rows of %d (%.1f s)" % (done, rows_total, el)}
+
+
+def suite(args):
+    """Every workload and mode, cold (rotating buffers) and warm (one pair),
+    each timed like the headline; the same-bytes copy; and the oracle on one
+    host thread and on all of them (up to 16)."""
+    import torch
+
+    import bilinear_image_resize_amd as R
+    from bilinear_image_resize_amd.workloads import WORKLOADS, make_source
+
+    dev = torch.device("cuda:0")
+    lib = R._load()
+    stream = torch.cuda.current_stream(dev)
+    hold = StreamHold(dev, stream)
+    cores = max(1, min(16, os.cpu_count() or 1))
+    for w in WORKLOADS.values():
+        src_np = make_source(w)
+        src0 = torch.from_numpy(src_np).to(dev)
+        tdt = src0.dtype
+        pairs = max(2, -(-2 * INFINITY_CACHE_BYTES // (w.src_bytes + w.dst_bytes)))
+        srcs = [src0] + [src0.clone() for _ in range(pairs - 1)]
+        dsts = [torch.empty(w.dst_shape, dtype=tdt, device=dev) for _ in range(pairs)]
+        sp = [t.data_ptr() for t in srcs]
+        dp = [t.data_ptr() for t in dsts]
+        code = R.U8 if w.dtype == "u8" else R.F32
+        for mode in w.modes:
+            entry = lib.resize_linear if mode == "linear" else lib.resize_nearest
+            bad = [0]
+
+            def cold(i, sh_):
+                j = i % pairs
+                bad[0] |= entry(sp[j], dp[j], w.batch, w.H, w.W, w.C, code, w.dH, w.dW, sh_)
+
+            def warm(i, sh_):
+                bad[0] |= entry(sp[0], dp[0], w.batch, w.H, w.W, w.C, code, w.dH, w.dW, sh_)
+
+            for i in range(3):
+                cold(i, stream.cuda_stream)
+            torch.cuda.synchronize(dev)
+            t_w = time.perf_counter()
+            for i in range(20):
+                cold(i, stream.cuda_stream)
+            enq = (time.perf_counter() - t_w) * 1e6 / 20
+            torch.cuda.synchronize(dev)
+            n = 300 if w.dst_pixels * w.C * w.itemsize < (64 << 20) else 100
+            ms_c, _, _ = timed_run(cold, n, [stream], hold, enq)
+            ms_w, _, _ = timed_run(warm, n, [stream], hold, enq)
+            if bad[0]:
+                raise R.ResizeError(bad[0], "resize")
+            b = w.src_bytes + w.dst_bytes
+            cp = copy_same_bytes(b, n, lib, dev, stream, hold, enq)
+            line = {"workload": w.name, "mode": mode, "bytes": b, "dst_pixels": w.dst_pixels,
+                    "cold": {"us": round(ms_c * 1e3, 3), "GBps": round(b / ms_c / 1e6, 1),
+                             "frac_of_peak": round(b / ms_c / 1e6 / HBM_PEAK_GBPS, 4),
+                             "Gpix_s": round(w.dst_pixels / ms_c / 1e6, 3), "pairs": pairs},
+                    "warm": {"us": round(ms_w * 1e3, 3), "GBps": round(b / ms_w / 1e6, 1),
+                             "Gpix_s": round(w.dst_pixels / ms_w / 1e6, 3)},
+                    "copy_same_bytes": cp}
+            if not args.no_cpu:
+                line["oracle_1_thread"] = oracle_rate(w, src_np, mode, 1, args.cpu_seconds / 2)
+                line["oracle_all_cores"] = oracle_rate(w, src_np, mode, cores, args.cpu_seconds / 2)
+                line["oracle_all_cores"]["host"] = "%d of %d threads (%s)" % (
+                    cores, os.cpu_count() or 1, host_cpu_model())
+            print(json.dumps(line), flush=True)
+        del srcs, dsts
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -244,6 +459,11 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args)
+        return
+    if args.ceiling:
+        ceiling()
+    if args.suite:
+        suite(args)
         return
 
     import numpy as np
@@ -336,63 +556,86 @@ def main():
     dp = [t.data_ptr() for t in dsts]
     N, H, W, C, dH, dW = w.batch, w.H, w.W, w.C, w.dH, w.dW
 
+    def launch(i, sh_):
+        j = i % pairs
+        return entry(sp[j], dp[j], N, H, W, C, code, dH, dW, sh_)
+
     def steps(k0, k):
         bad = 0
         for i in range(k0, k0 + k):
-            j = i % pairs
-            bad |= entry(sp[j], dp[j], N, H, W, C, code, dH, dW, sh)
+            bad |= launch(i, sh)
         if bad:
             raise R.ResizeError(bad, "resize")
 
-    steps(0, args.warmup)
+    # first calls (library and code object loading), then the host's call rate
+    steps(0, 3)
     torch.cuda.synchronize(dev)
-
-    # timed region: exactly K steps, bracketed by synchronisation, with a HIP
-    # event pair on the launch stream around the whole region
+    t_w = time.perf_counter()
+    steps(3, 8)
+    enqueue_us = (time.perf_counter() - t_w) * 1e6 / 8
+    torch.cuda.synchronize(dev)
+    hold = StreamHold(dev, stream)
     K = args.steps
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    bad = [0]
+
+    def launch_checked(i, sh_):
+        bad[0] |= launch(args.warmup + i, sh_)
+
+    def launch_warmup(i, sh_):
+        bad[0] |= launch(i, sh_)
+
+    # Warm-up, then the timed region.  The W warm-up steps are queued behind
+    # the stream hold directly ahead of the K timed steps, so the timed steps
+    # start in the steady state of a running queue; the HIP event pair on
+    # the launch stream brackets exactly the K timed steps, and
+    # synchronisation brackets the whole region.
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    e0.record(stream)
-    steps(args.warmup, K)
-    e1.record(stream)
-    t_enq = time.perf_counter()
+    ker_avg_ms, t_enq, hold_ok = timed_run(launch_checked, K, [stream], hold, enqueue_us,
+                                           pre=(launch_warmup, args.warmup))
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    ker_avg_ms = e0.elapsed_time(e1) / K
+    if bad[0]:
+        raise R.ResizeError(bad[0], "resize")
 
-    ms_per_step = wall * 1e3 / K
+    ms_per_step = ker_avg_ms
     gpix = w.dst_pixels / (ms_per_step * 1e-3) / 1e9
     alg_bytes = pair_bytes                    # src read once + dst written once
     achieved = alg_bytes / (ker_avg_ms * 1e-3) / 1e9
 
-    # Informational: the same K frames with consecutive calls alternating over
-    # two HIP streams (default priority), as a pipeline of independent frames
-    # would issue them; one frame's launch ramp and drain overlap the next
-    # frame's.  Not the headline: per-kernel durations overlap here.
+    # Informational: frames issued round-robin over several HIP streams
+    # (default priority), as a pipeline of independent frames would issue
+    # them: one frame's launch ramp and drain overlap the next frame's.
+    # Timed like the headline (held, HIP events, joined over the streams),
+    # over at least 300 frames.  Not the headline: kernels overlap here.
     pipelined = None
     if not args.no_pipelined:
-        side = [stream, torch.cuda.Stream(dev)]
-        shs = [t.cuda_stream for t in side]
+        n_s = max(K, 300)
+        side = [stream] + [torch.cuda.Stream(dev) for _ in range(max(1, args.streams) - 1)]
+        ms2, _, hold2 = timed_run(launch_checked, n_s, side, hold, enqueue_us)
+        if bad[0]:
+            raise R.ResizeError(bad[0], "resize")
+        pipelined = {"streams": len(side), "frames": n_s, "us_per_frame": round(ms2 * 1e3, 3),
+                     "Gpix_s": round(w.dst_pixels / (ms2 * 1e-3) / 1e9, 3),
+                     "GBps": round(pair_bytes / (ms2 * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(pair_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "timing": "HIP events over %d frames, streams held until all were enqueued"
+                               % n_s}
 
-        def steps2(k0, k):
-            bad = 0
-            for i in range(k0, k0 + k):
-                j = i % pairs
-                bad |= entry(sp[j], dp[j], N, H, W, C, code, dH, dW, shs[i & 1])
-            if bad:
-                raise R.ResizeError(bad, "resize")
+    # Informational: the same launch on one buffer pair (cache-resident
+    # source and destination: warm)
+    warm = None
+    if not args.warm and not args.no_warm:
+        n_w = max(K, 300)
+        def launch_warm(i, sh_):
+            bad[0] |= entry(sp[0], dp[0], N, H, W, C, code, dH, dW, sh_)
 
-        steps2(0, args.warmup)
-        torch.cuda.synchronize(dev)
-        t0p = time.perf_counter()
-        steps2(args.warmup, K)
-        torch.cuda.synchronize(dev)
-        wall2 = time.perf_counter() - t0p
-        pipelined = {"streams": 2, "us_per_frame": round(wall2 * 1e6 / K, 3),
-                     "Gpix_s": round(w.dst_pixels * K / wall2 / 1e9, 3),
-                     "GBps": round(pair_bytes * K / wall2 / 1e9, 1)}
+        ms3, _, _ = timed_run(launch_warm, n_w, [stream], hold, enqueue_us)
+        if bad[0]:
+            raise R.ResizeError(bad[0], "resize")
+        warm = {"launches": n_w, "kernel_us": round(ms3 * 1e3, 3),
+                "GBps": round(pair_bytes / (ms3 * 1e-3) / 1e9, 1),
+                "Gpix_s": round(w.dst_pixels / (ms3 * 1e-3) / 1e9, 3)}
 
     # Informational: B steps captured once into a HIP graph and replayed, which
     # removes the per-call host cost that bounds tiny images.
@@ -470,9 +713,14 @@ def main():
             "batch": w.batch, "src_hwc": [w.H, w.W, w.C], "dst_hw": [w.dH, w.dW],
             "mode": mode, "cache": "warm (1 pair)" if args.warm else "cold (%d rotating pairs)" % pairs,
         },
-        "hbm_GBps_wall": round(pair_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "timing": "HIP events around the K steps on the launch stream, held until the W warm-up "
+                  "and K timed steps were enqueued (headline, roofline); wall clock of the "
+                  "synchronised region beside it",
         "kernel_us": round(ker_avg_ms * 1e3, 3),
-        "host_enqueue_us": round((t_enq - t0) * 1e6 / K, 3),
+        "hbm_GBps": round(achieved, 1),
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "host_enqueue_us": round(t_enq * 1e6 / K, 3),
+        "hold_covered_enqueue": bool(hold_ok),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -482,6 +730,10 @@ def main():
             "traffic": traffic,
         },
     }
+    entry_t = MEASURED_TRAFFIC.get((w.name, mode))
+    if traffic is not None:
+        line["traffic_source"] = {"profile": entry_t["profile"], "kernel": entry_t["kernel"],
+                                  "counters": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE"}
     # the measurement of "From Prototype to Performance" ("Measure
     # performance carefully"): launches timed one by one with HIP events,
     # sorted, 10 % trimmed at each end, averaged (informational)
@@ -490,15 +742,15 @@ def main():
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(R_)]
         torch.cuda.synchronize(dev)
-        bad = 0
+        badt = 0
         for i, (ea, eb) in enumerate(evs):
             j = i % pairs
             ea.record(stream)
-            bad |= entry(sp[j], dp[j], N, H, W, C, code, dH, dW, sh)
+            badt |= entry(sp[j], dp[j], N, H, W, C, code, dH, dW, sh)
             eb.record(stream)
         torch.cuda.synchronize(dev)
-        if bad:
-            raise R.ResizeError(bad, "resize")
+        if badt:
+            raise R.ResizeError(badt, "resize")
         d = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
         cut = R_ // 10
         kept = d[cut:R_ - cut]
@@ -508,15 +760,16 @@ def main():
     # the copy-kernel ceiling at the same bytes per launch, and the HBM peak
     # the runtime reports (both informational)
     if not args.no_copy:
-        cp = copy_same_bytes(pair_bytes, min(K, 500), R._load(), dev,
-                             torch.cuda.current_stream(dev).cuda_stream)
+        cp = copy_same_bytes(pair_bytes, max(K, 300), R._load(), dev, stream, hold, enqueue_us)
         cp["resize_frac_of_copy"] = round(achieved / cp["GBps"], 4)
         line["copy_same_bytes"] = cp
     peak_dev = device_hbm_peak()
     if peak_dev:
         line["hbm_peak_device"] = peak_dev
     if pipelined:
-        line["pipelined_two_streams"] = pipelined
+        line["sustained"] = pipelined
+    if warm:
+        line["warm"] = warm
     if graphed:
         line["graph_replay"] = graphed
     if not args.no_cpu and args.op == "resize":

@@ -10,6 +10,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmi_resize.so")
 SOURCES = [os.path.join(CSRC, "resize_abi.hip")]
+# measurement program (launch and bandwidth ceilings), linked against the
+# library; bench.py --ceiling runs it
+CEILING_SRC = os.path.join(CSRC, "ceiling.hip")
+CEILING = os.path.join(PKG, "mi_resize_ceiling")
 DEPENDS = SOURCES + [os.path.join(CSRC, "resize_kernels.hpp"),
                      os.path.join(ROOT, "include", "mi_resize.h")]
 
@@ -30,18 +34,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the HIP sources into bilinear_image_resize_amd/libmi_resize.so."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+def _compile(cmd, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = cmd + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     try:
         subprocess.check_call(cmd)
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         if os.path.exists(tmp):
             os.remove(tmp)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the HIP sources into bilinear_image_resize_amd/libmi_resize.so,
+    then the ceiling measurement program linked against it."""
+    _compile([HIPCC] + FLAGS + SOURCES, LIB, verbose)
+    exe_flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    _compile([HIPCC] + exe_flags + [CEILING_SRC, "-L", PKG, "-lmi_resize",
+                                    "-Wl,-rpath,$ORIGIN"], CEILING, verbose)
     return LIB
 
 
