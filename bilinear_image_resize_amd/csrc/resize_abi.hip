@@ -306,8 +306,13 @@ bool try_rowseg_px(const void *src, void *dst, int batch, int H, int W, int dH, 
         // at most 4 x (16 KiB of slots + 4 KiB of output staging) = 80 KiB,
         // within the 160 KiB one gfx950 workgroup may use
         static_assert(kSegWaves * (kSegLdsBudget + nstage) <= 160 * 1024, "LDS per workgroup");
+        // plus the segment's column table where the kernel builds one in LDS
+        constexpr int table_bytes = !ROI && PX >= 4 ? kSegLanes * PX * (sizeof(T) == 1 ? 4 : 8) : 0;
+        static_assert(kSegWaves * (kSegLdsBudget + nstage) + table_bytes <= 160 * 1024,
+                      "LDS per workgroup with the column table");
         const int lds_bytes = kSegWaves * (2 * slot_bytes +
-                                           (nstage > 0 && seg_nhwc_staged(dst, dW, C) ? nstage : 0));
+                                           (nstage > 0 && seg_nhwc_staged(dst, dW, C) ? nstage : 0)) +
+                              table_bytes;
         return launch(kernel, pl.grid, dim3(kSegLanes * kSegWaves), lds_bytes, st,
                       (const T *)src, dst,
                       H, W, dH, dW, rows, pl.rows_per_block, pl.seg_cap,
@@ -465,14 +470,19 @@ int launch_up2_u8(const void *src, void *dst, int batch, int H, int W, hipStream
                       dim3(64, RB), 0, st, (const uint8_t *)src, (uint8_t *)dst, W, rows,
                       chunks_per_row);
     } else {
-        // H + 1 gaps per image (H <= 32767 since dH <= 65535); images
-        // beyond the grid's z extent are strided
+        // H + 1 gaps per image (H <= 32767 since dH <= 65535); a 1-D grid
+        // of gx * gy * gz workgroups (at most 2^24, so blocks x threads stays
+        // below 2^32), images beyond gz strided
         const long long gx = (chunks_per_row + 63) / 64, gy = (H + RB) / RB;
         long long gz = batch < kMaxGridY ? batch : kMaxGridY;
-        if (gx * gy * gz > kMaxGroups) gz = kMaxGroups / (gx * gy);
-        return launch(linear_up2_u8<C, RB>, dim3((unsigned)gx, (unsigned)gy, (unsigned)gz),
-                      dim3(64, RB), 0, st, (const uint8_t *)src, (uint8_t *)dst, H, W, batch,
-                      chunks_per_row, make_div_by((unsigned)gx), make_div_by((unsigned)gy));
+        if (gx * gy * gz > kMaxGridX) gz = kMaxGridX / (gx * gy);
+        // one image: no image arithmetic in the prologue, whose scalar work
+        // all resident waves queue for (1080p grey 3.65 -> 3.49 us)
+        auto kernel = batch == 1 ? linear_up2_u8<C, RB, true> : linear_up2_u8<C, RB, false>;
+        return launch(kernel, dim3((unsigned)(gx * gy * gz)), dim3(64 * RB), 0, st,
+                      (const uint8_t *)src, (uint8_t *)dst, H, W, batch, chunks_per_row,
+                      (unsigned)gx, (unsigned)gy, (unsigned)gz, make_div_by((unsigned)gx),
+                      make_div_by((unsigned)gy));
     }
 }
 
