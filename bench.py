@@ -13,14 +13,17 @@ steps), the kernel's HBM roofline (algorithmic bytes = src read once + dst
 written once, over the kernel's average duration), and the CPU oracle timed
 on the host cores as a reported baseline.
 
-Timing protocol of the headline: a bounded spin kernel (torch.cuda._sleep)
-holds the launch stream while the host enqueues the W warm-up steps and the K
-timed steps behind it, and a HIP event pair on that stream around the K
-timed steps gives their GPU time; synchronisation brackets the region.  The
-steps then run back to back as in a pipeline, starting in its steady state,
-and neither the host's call rate nor its synchronisation latency enters
-`value`.  The wall clock of the synchronised region (hold, warm-up and
-synchronisation included) is reported beside it.
+Timing protocol of the headline: the W warm-up steps are queued directly
+ahead of the K timed steps, and a HIP event pair on the launch stream around
+the K timed steps gives their GPU time; synchronisation brackets the region.
+A bounded spin kernel (torch.cuda._sleep) holds the stream while the host
+enqueues: the whole run when a step is shorter than twice the host's call
+time (the GPU would otherwise outrun the host), else only the first steps.
+Before any of this, untimed steps run until 50 ms of GPU work have passed
+(the first milliseconds after the set-up run slower).  The steps then run
+back to back as in a pipeline, starting in its steady state, and neither the
+host's call rate nor its synchronisation latency enters `value`.  The wall clock of the synchronised region (hold, warm-up
+and synchronisation included) is reported beside it.
 `sustained` (informational) times frames issued round-robin over several
 HIP streams the same way.
 
@@ -207,22 +210,28 @@ class StreamHold:
             self.torch.cuda._sleep(int(us * self.cycles_per_us))
 
 
-def timed_run(launch, n, streams, hold, enqueue_us, pre=None):
+def timed_run(launch, n, streams, hold, enqueue_us, pre=None, full_hold=True):
     """GPU time per launch (ms) of n launches, launch(i, stream_handle) for
-    i in [0, n) on streams[i % S], held until all are enqueued, timed by a
-    HIP event pair on streams[0] joined with every other stream.  `pre`, if
-    given, is (launch function, count): untimed launches queued behind the
-    hold directly ahead of the timed ones, on streams[0], so that the timed
+    i in [0, n) on streams[i % S], timed by a HIP event pair on streams[0]
+    joined with every other stream.  A bounded spin kernel first holds
+    streams[0]: for the whole enqueue (full_hold: launches shorter than the
+    host's call, which the GPU would otherwise outrun), or for the first 30
+    (longer launches: the host stays ahead once they run, and holding a
+    long queue measured up to 4 % slower for them).  `pre`, if given, is
+    (launch function, count): untimed launches queued behind the hold
+    directly ahead of the timed ones, on streams[0], so that the timed
     launches start in the steady state of a running queue.  Returns (ms per
-    launch, host enqueue seconds, whether the hold outlasted the enqueue)."""
+    launch, host enqueue seconds, whether the hold outlasted the enqueue of
+    the launches it was meant to cover)."""
     import torch
     main = streams[0]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     n_pre = pre[1] if pre else 0
+    covered = n_pre + (n if full_hold else min(n, 30))
     # about 1.5x the host's enqueue time, capped at one second (a slow host,
     # e.g. under a tracing profiler, then shows as hold_covered_enqueue false)
-    hold_us = min(1.5 * (n + n_pre) * enqueue_us + 100.0, 1e6)
+    hold_us = min(1.5 * covered * enqueue_us + 100.0, 1e6)
     handles = [st.cuda_stream for st in streams]
     t0 = time.perf_counter()
     hold(main, hold_us)
@@ -240,7 +249,38 @@ def timed_run(launch, n, streams, hold, enqueue_us, pre=None):
     e1.record(main)
     t_enq = time.perf_counter() - t0
     e1.synchronize()
-    return e0.elapsed_time(e1) / n, t_enq, t_enq * 1e6 < hold_us
+    return e0.elapsed_time(e1) / n, t_enq, t_enq * covered / (n + n_pre) * 1e6 < hold_us
+
+
+def settle(launch, stream, min_ms=50.0, max_launches=20000):
+    """Untimed launches until at least min_ms of GPU work has run.  The
+    first few milliseconds of work after the set-up (buffers just written,
+    the GPU idle since) run up to 20 % slower on this hardware - a 300-launch
+    run of the thumbnail batch averaged 54.5 us where the next one took 45
+    - so the timed launches start only after this.  Returns the launch
+    count."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    done, batch = 0, 8
+    e0.record(stream)
+    while done < max_launches:
+        for i in range(batch):
+            launch(done + i, stream.cuda_stream)
+        done += batch
+        e1.record(stream)
+        e1.synchronize()
+        if e0.elapsed_time(e1) >= min_ms:
+            break
+        batch = min(2 * batch, 512)
+    return done
+
+
+def needs_full_hold(launch, stream, hold, enqueue_us):
+    """Whether launches are short enough (under twice the host's call time)
+    that the whole timed run must be held: estimated from 12 held launches."""
+    ms, _, _ = timed_run(launch, 12, [stream], hold, enqueue_us)
+    return ms * 1e3 < 2.0 * enqueue_us
 
 
 def copy_same_bytes(total_bytes, steps, lib, dev, stream, hold, enqueue_us):
@@ -260,10 +300,10 @@ def copy_same_bytes(total_bytes, steps, lib, dev, stream, hold, enqueue_us):
     def launch(i, sh):
         bad[0] |= lib.resize_copy_bytes(ptrs[i % pairs][0], ptrs[i % pairs][1], n, sh)
 
-    for i in range(2 * pairs):
-        launch(i, stream.cuda_stream)
-    torch.cuda.synchronize(dev)
-    ms, _, _ = timed_run(launch, steps, [stream], hold, enqueue_us)
+    settle(launch, stream)
+    full = needs_full_hold(launch, stream, hold, enqueue_us)
+    ms, _, _ = timed_run(launch, steps, [stream], hold, enqueue_us, pre=(launch, 10),
+                         full_hold=full)
     if bad[0]:
         raise RuntimeError("resize_copy_bytes failed (%d)" % bad[0])
     us = ms * 1e3
@@ -355,33 +395,43 @@ def ceiling():
 
 
 def oracle_rate(w, src_np, mode, threads, budget_s):
-    """Oracle Gpix/s on `threads` host threads over consecutive bands of
-    output rows (wrapping around the batch), for about budget_s seconds."""
+    """Oracle Gpix/s on `threads` host threads for about budget_s seconds.
+    Each round gives every thread its own run of consecutive output rows
+    (wrapping around the batch), sized to about 0.2 s of single-thread work
+    from a first timed band, so thread start-up stays negligible."""
     import oracle
 
     fn = oracle.resize_linear if mode == "linear" else oracle.resize_nearest
     fn(src_np[:1], 1, 1)
     rows_total = w.batch * w.dH
-    band = max(threads, min(rows_total, max(1, 200000 // w.dW)))
+    probe = max(1, min(rows_total, 20000 // w.dW + 1))
+    t = time.perf_counter()
+    fn(src_np, w.dH, w.dW, rows=(0, probe))
+    s_per_row = max(1e-9, (time.perf_counter() - t) / probe)
+    per = max(1, min(rows_total // threads if rows_total >= threads else 1, int(0.2 / s_per_row)))
     done, r0 = 0, 0
     t0 = time.perf_counter()
     while True:
-        r1 = min(rows_total, r0 + band)
-        bounds = [r0 + (r1 - r0) * k // threads for k in range(threads + 1)]
-        ts = [threading.Thread(target=fn, args=(src_np, w.dH, w.dW),
-                               kwargs={"rows": (bounds[k], bounds[k + 1])})
-              for k in range(threads) if bounds[k + 1] > bounds[k]]
-        for t in ts:
-            t.start()
-        for t in ts:
-            t.join()
-        done += r1 - r0
-        r0 = 0 if r1 == rows_total else r1
+        spans = []
+        for _ in range(threads):
+            if r0 >= rows_total:
+                r0 = 0
+            r1 = min(rows_total, r0 + per)
+            spans.append((r0, r1))
+            r0 = r1
+        ts = [threading.Thread(target=fn, args=(src_np, w.dH, w.dW), kwargs={"rows": sp})
+              for sp in spans]
+        for t_ in ts:
+            t_.start()
+        for t_ in ts:
+            t_.join()
+        done += sum(b - a for a, b in spans)
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     return {"Gpix_s": round(done * w.dW / el / 1e9, 5), "threads": threads,
-            "sample": "%d output rows of %d (%.1f s)" % (done, rows_total, el)}
+            "sample": "%d output rows of %d, %d per thread per round (%.1f s)" % (
+                done, rows_total, per, el)}
 
 
 def suite(args):
@@ -428,8 +478,10 @@ def suite(args):
             enq = (time.perf_counter() - t_w) * 1e6 / 20
             torch.cuda.synchronize(dev)
             n = 300 if w.dst_pixels * w.C * w.itemsize < (64 << 20) else 100
-            ms_c, _, _ = timed_run(cold, n, [stream], hold, enq)
-            ms_w, _, _ = timed_run(warm, n, [stream], hold, enq)
+            settle(cold, stream)
+            full = needs_full_hold(cold, stream, hold, enq)
+            ms_c, _, _ = timed_run(cold, n, [stream], hold, enq, pre=(cold, 10), full_hold=full)
+            ms_w, _, _ = timed_run(warm, n, [stream], hold, enq, pre=(warm, 10), full_hold=full)
             if bad[0]:
                 raise R.ResizeError(bad[0], "resize")
             b = w.src_bytes + w.dst_bytes
@@ -589,10 +641,12 @@ def main():
     # start in the steady state of a running queue; the HIP event pair on
     # the launch stream brackets exactly the K timed steps, and
     # synchronisation brackets the whole region.
+    settled = settle(launch_warmup, stream)
+    full_hold = needs_full_hold(launch_warmup, stream, hold, enqueue_us)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     ker_avg_ms, t_enq, hold_ok = timed_run(launch_checked, K, [stream], hold, enqueue_us,
-                                           pre=(launch_warmup, args.warmup))
+                                           pre=(launch_warmup, args.warmup), full_hold=full_hold)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     if bad[0]:
@@ -630,7 +684,8 @@ def main():
         def launch_warm(i, sh_):
             bad[0] |= entry(sp[0], dp[0], N, H, W, C, code, dH, dW, sh_)
 
-        ms3, _, _ = timed_run(launch_warm, n_w, [stream], hold, enqueue_us)
+        ms3, _, _ = timed_run(launch_warm, n_w, [stream], hold, enqueue_us,
+                              pre=(launch_warm, 10), full_hold=full_hold)
         if bad[0]:
             raise R.ResizeError(bad[0], "resize")
         warm = {"launches": n_w, "kernel_us": round(ms3 * 1e3, 3),
@@ -720,6 +775,8 @@ def main():
         "hbm_GBps": round(achieved, 1),
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "host_enqueue_us": round(t_enq * 1e6 / K, 3),
+        "settle_launches": settled,
+        "hold": "whole run" if full_hold else "first 30 launches",
         "hold_covered_enqueue": bool(hold_ok),
         "roofline": {
             "bound": "hbm",
