@@ -55,10 +55,25 @@ INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 # traffic when they no longer hash to that value (the kernel changed since).
 MEASURED_TRAFFIC = {
     ("4k", "linear"): {"kernel": "linear_half_u8<3, false, false>",
-                       "profile": "profiles/linear_half_u8_4k_rgb_pmc_traffic.md",
-                       "kernel_source_sha256_16": "716059118abe56e4",
-                       "fetch_kib": 12176.86, "write_kib": 6075.0,
-                       "fetch_scale": 1.99833, "write_scale": 0.99911},
+                       "profile": "profiles/pmc_traffic_all_workloads.md",
+                       "kernel_source_sha256_16": "ab9b1ca7fd37c13b",
+                       "fetch_kib": 12173.032, "write_kib": 6075.0,
+                       "fetch_scale": 1.99833, "write_scale": 0.99893},
+    ("up2x", "linear"): {"kernel": "linear_up2_u8<1, 4, true>",
+                         "profile": "profiles/pmc_traffic_all_workloads.md",
+                         "kernel_source_sha256_16": "ab9b1ca7fd37c13b",
+                         "fetch_kib": 1042.603, "write_kib": 8100.0,
+                         "fetch_scale": 1.99833, "write_scale": 0.99893},
+    ("thumb", "linear"): {"kernel": "rowseg<unsigned char, 3, false, 2, true, 0, false, 0, 0>",
+                          "profile": "profiles/pmc_traffic_all_workloads.md",
+                          "kernel_source_sha256_16": "ab9b1ca7fd37c13b",
+                          "fetch_kib": 107586.509, "write_kib": 38685.668,
+                          "fetch_scale": 1.99833, "write_scale": 0.99893},
+    ("rgbaf", "linear"): {"kernel": "rowseg<float, 4, false, 4, false, 0, false, 0, 0>",
+                          "profile": "profiles/pmc_traffic_all_workloads.md",
+                          "kernel_source_sha256_16": "ab9b1ca7fd37c13b",
+                          "fetch_kib": 320212.78, "write_kib": 296627.09,
+                          "fetch_scale": 1.99856, "write_scale": 0.99893},
 }
 
 
@@ -106,6 +121,10 @@ def parse():
                    help="skip the copy-kernel ceiling at the same bytes per launch")
     p.add_argument("--no-pipelined", "--no-sustained", dest="no_pipelined", action="store_true",
                    help="skip the informational multi-stream (sustained) measurement")
+    p.add_argument("--hold", default="auto", choices=["auto", "whole", "first"],
+                   help="stream hold of the timed run: auto (the whole run for launches shorter "
+                        "than twice the host's call time, else the first 30), whole (one second, "
+                        "for a tracing profiler, which slows every call), first")
     p.add_argument("--no-warm", action="store_true",
                    help="skip the informational warm-cache figure")
     p.add_argument("--streams", type=int, default=3,
@@ -210,7 +229,7 @@ class StreamHold:
             self.torch.cuda._sleep(int(us * self.cycles_per_us))
 
 
-def timed_run(launch, n, streams, hold, enqueue_us, pre=None, full_hold=True):
+def timed_run(launch, n, streams, hold, enqueue_us, pre=None, full_hold=True, hold_us_min=0.0):
     """GPU time per launch (ms) of n launches, launch(i, stream_handle) for
     i in [0, n) on streams[i % S], timed by a HIP event pair on streams[0]
     joined with every other stream.  A bounded spin kernel first holds
@@ -231,7 +250,7 @@ def timed_run(launch, n, streams, hold, enqueue_us, pre=None, full_hold=True):
     covered = n_pre + (n if full_hold else min(n, 30))
     # about 1.5x the host's enqueue time, capped at one second (a slow host,
     # e.g. under a tracing profiler, then shows as hold_covered_enqueue false)
-    hold_us = min(1.5 * covered * enqueue_us + 100.0, 1e6)
+    hold_us = min(max(1.5 * covered * enqueue_us + 100.0, hold_us_min), 1e6)
     handles = [st.cuda_stream for st in streams]
     t0 = time.perf_counter()
     hold(main, hold_us)
@@ -642,11 +661,13 @@ def main():
     # the launch stream brackets exactly the K timed steps, and
     # synchronisation brackets the whole region.
     settled = settle(launch_warmup, stream)
-    full_hold = needs_full_hold(launch_warmup, stream, hold, enqueue_us)
+    full_hold = (args.hold == "whole" or
+                 (args.hold == "auto" and needs_full_hold(launch_warmup, stream, hold, enqueue_us)))
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     ker_avg_ms, t_enq, hold_ok = timed_run(launch_checked, K, [stream], hold, enqueue_us,
-                                           pre=(launch_warmup, args.warmup), full_hold=full_hold)
+                                           pre=(launch_warmup, args.warmup), full_hold=full_hold,
+                                           hold_us_min=1e6 if args.hold == "whole" else 0.0)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     if bad[0]:
