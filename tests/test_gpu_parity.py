@@ -169,8 +169,11 @@ def test_half_downscale_random_shapes(C):
 @pytest.mark.parametrize("C", [1, 3, 4])
 def test_double_upscale_shapes(C):
     r = np.random.default_rng(91 + C)
+    # (1, 3, 4) and (2, 2, 4): for 4 channels a row of a single chunk, which
+    # the linear 2x kernel loads without its one-load window; W = 2 chunks
+    # (16 px for 1 and 3 channels, 8 for 4) has only a start and an end lane
     for (N, H, W) in ((1, 1, 16), (2, 3, 32), (3, 17, 48), (1, 64, 1920), (1, 2, 8), (1, 1, 1),
-                      (2, 5, 24), (1, 9, 17), (4, 1, 160)):
+                      (2, 5, 24), (1, 9, 17), (4, 1, 160), (1, 3, 4), (2, 2, 4)):
         s = random_image(r, (N, H, W, C), "u8")
         for mode in ("linear", "nearest"):
             say("case up2 %s C=%d N=%d src=%dx%d" % (mode, C, N, H, W))
