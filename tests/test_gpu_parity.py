@@ -445,6 +445,28 @@ def test_side_stream_and_hwc():
     assert_parity(out2.cpu().numpy()[None], oracle.resize_nearest(s_np, 240, 320), "scale")
 
 
+def test_frames_round_robin_over_streams():
+    """Frames issued round-robin on three streams, so that consecutive
+    launches overlap on the GPU (the sustained configuration the benchmark
+    times): every frame's output must still equal the oracle's.  Distinct
+    seeded 4K-shaped frames (2:1 kernel) and 1080p grey frames (2x kernel),
+    each into its own output buffer."""
+    r = np.random.default_rng(3131)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(2)]
+    for (H, W, C, dH, dW) in ((2160, 3840, 3, 1080, 1920), (540, 960, 1, 1080, 1920)):
+        frames = [random_image(r, (1, H, W, C), "u8") for _ in range(6)]
+        srcs = [torch.from_numpy(f).cuda() for f in frames]
+        outs = [torch.empty((1, dH, dW, C), dtype=torch.uint8, device="cuda") for _ in frames]
+        torch.cuda.synchronize()
+        say("case round-robin streams %s -> %s" % ((H, W, C), (dH, dW)))
+        for i, (sv, ov) in enumerate(zip(srcs, outs)):
+            R.resize_linear(sv, ov, stream=streams[i % 3])
+        torch.cuda.synchronize()
+        for i, f in enumerate(frames):
+            assert_parity(outs[i].cpu().numpy(), oracle.resize_linear(f, dH, dW),
+                          "round-robin frame %d %s" % (i, (H, W, C)))
+
+
 def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         R.resize(torch.zeros(4, 4, 3, dtype=torch.uint8), (2, 2))          # host tensor
