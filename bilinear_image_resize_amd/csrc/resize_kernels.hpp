@@ -220,6 +220,42 @@ __device__ __forceinline__ unsigned blend_u8(unsigned p00, unsigned p01, unsigne
     return (__umul24(wy0, top) + __umul24(wy1, bot) + (1u << 21)) >> 22;
 }
 
+// The same blend on tap pairs, for kernels that hold each row's two taps of
+// a channel as 16-bit halves of one register (tap a low, tap b high) and
+// the column weights as the pair (2048 - u, u): one unsigned 16-bit dot
+// product per row gives wx0 p_a + wx1 p_b <= 2048 * 255 exactly, and the
+// row sums are combined with the row weights scaled by 4, so that
+//   4 (wy0 top + wy1 bot) + 2^23 = 4 (sum + 2^21) < 2^32
+// carries the rounded result, floor((sum + 2^21) / 2^22), in bits 24..31:
+// a byte permute then packs it with no shift.  Where both taps are one
+// column the pair (2048, 0) gives 2048 p_a, as the scalar form does.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t blend_u8_pairs(uint32_t pa, uint32_t pb, uint32_t wx,
+                                                   uint32_t wy0x4, uint32_t wy1x4)
+{
+    const uint32_t top = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2_t, pa),
+                                                __builtin_bit_cast(u16x2_t, wx), 0u, false);
+    const uint32_t bot = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2_t, pb),
+                                                __builtin_bit_cast(u16x2_t, wx), 0u, false);
+    return __umul24(wy0x4, top) + __umul24(wy1x4, bot) + (1u << 23);
+}
+
+// Column weight pair of blend_u8_pairs: (2048 - u, u), or (2048, 0) where
+// tap b is not the next column.
+__device__ __forceinline__ uint32_t weight_pair(unsigned u, bool next)
+{
+    return next ? (2048u - u) | (u << 16) : 2048u;
+}
+
+// Byte 3 of each of four words, packed into one word (first word lowest).
+__device__ __forceinline__ uint32_t pack_byte3(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0703u);
+    const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x0c0c0703u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 __device__ __forceinline__ float blend_f32(float p00, float p01, float p10, float p11,
                                            float wx, float wy)
 {
@@ -1439,13 +1475,14 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
 
     // This lane's column table: byte offset of tap a from column sa, whether
     // tap b is the next column (it is not only where both taps clamp to the
-    // last column), and the weight of tap b.  Recomputed when a crop changes
+    // last column), and the weights: for uint8 the pair (2048 - u, u), or
+    // (2048, 0) where tap b is tap a, for float u.  Recomputed when a crop changes
     // with the image.  The lane's first column is mapped with one division;
     // the next ones step from it exactly (the numerator grows by 2 n_in per
     // column), and columns past the last output column repeat it.
     int toff[PX];
     bool tnext[PX];
-    unsigned tw[PX];
+    uint32_t twp[PX];
     float twf[PX];
     auto lane_table = [&](const Crop &c, int sa) {
         AxisStepper xs;
@@ -1460,7 +1497,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                 const int k = xs.q;
                 toff[p] = (min(k, last) - sa) * PB;
                 tnext[p] = false;
-                tw[p] = 0;
+                twp[p] = 0;
                 twf[p] = 0.f;
             } else {
                 int a, b, rr;
@@ -1471,7 +1508,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                 Tap t;
                 t.r = rr;
                 t.den = xs.den;
-                if constexpr (sizeof(T) == 1) tw[p] = weight11(t);
+                if constexpr (sizeof(T) == 1) twp[p] = weight_pair(weight11(t), b != a);
                 else twf[p] = weightf(t);
             }
         }
@@ -1627,7 +1664,7 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             const uint32_t e0 = ctab[(lane * PX + p) * TWORDS];
             toff[p] = (int)(e0 >> 13);
             tnext[p] = (e0 >> 12) & 1u;
-            tw[p] = e0 & 4095u;
+            twp[p] = weight_pair(e0 & 4095u, (e0 >> 12) & 1u);
             if constexpr (TWORDS == 2) twf[p] = __builtin_bit_cast(float, ctab[(lane * PX + p) * TWORDS + 1]);
         }
     } else {
@@ -1663,6 +1700,11 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
 
         T res[PX * C];
         T resg[PX];                   // kOutGrey: one grey value per pixel
+        // uint8 linear: each result in bits 24..31 of a word (blend_u8_pairs)
+        constexpr bool U8LIN = sizeof(T) == 1 && !NEAREST;
+        static_assert(!U8LIN || (PX * C) % 4 == 0, "whole words of results");
+        [[maybe_unused]] uint32_t fx[U8LIN ? (OUT == kOutGrey ? PX : PX * C) : 1];
+        [[maybe_unused]] const uint32_t wy0x4 = (2048u - wy1) << 2, wy1x4 = wy1 << 2;
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
             if constexpr (NEAREST) {
@@ -1686,40 +1728,45 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                 // [PB, 2 PB); uint8 taps come in one 4- or 8-byte word so the
                 // read issues as a single (unaligned) LDS access.
                 if constexpr (sizeof(T) == 1) {
-                    // tap a = bytes [0, C), tap b = bytes [C, 2C) of the word
-                    // (or tap a again where both taps clamp to one column)
-                    uint32_t a_lo, a_hi, b_lo, b_hi;
+                    // Each channel's two taps of a row as the 16-bit halves
+                    // of one register (blend_u8_pairs).  Where tap b is not
+                    // the next column its weight is 0, so the byte read
+                    // there (inside the slot's read slack) does not count.
+                    uint32_t pa[OUT == kOutGrey ? 1 : C], pb[OUT == kOutGrey ? 1 : C];
                     if constexpr (C == 1) {
                         // two byte reads beat one shifted dword pair here
-                        const uint8_t *pa = la + toff[p], *pb = lb + toff[p];
-                        a_lo = a_hi = (uint32_t)pa[0] | ((uint32_t)pa[1] << 8);
-                        b_lo = b_hi = (uint32_t)pb[0] | ((uint32_t)pb[1] << 8);
-                    } else if constexpr (2 * PB <= 4) {
-                        a_lo = a_hi = lds_bytes4(la + toff[p]);
-                        b_lo = b_hi = lds_bytes4(lb + toff[p]);
+                        const uint8_t *qa = la + toff[p], *qb = lb + toff[p];
+                        pa[0] = (uint32_t)qa[0] | ((uint32_t)qa[1] << 16);
+                        pb[0] = (uint32_t)qb[0] | ((uint32_t)qb[1] << 16);
                     } else {
+                        // tap a = bytes [0, C), tap b = bytes [C, 2C)
+                        uint32_t a_lo, a_hi, b_lo, b_hi;
                         lds_bytes8(la + toff[p], a_lo, a_hi);
                         lds_bytes8(lb + toff[p], b_lo, b_hi);
+                        if constexpr (OUT == kOutGrey) {
+                            auto gr = [](uint32_t w) {
+                                return grey_u8(w & 255u, (w >> 8) & 255u, (w >> 16) & 255u);
+                            };
+                            const uint32_t a2 = C == 4 ? a_hi : __builtin_amdgcn_alignbyte(a_hi, a_lo, C);
+                            const uint32_t b2 = C == 4 ? b_hi : __builtin_amdgcn_alignbyte(b_hi, b_lo, C);
+                            pa[0] = gr(a_lo) | (gr(a2) << 16);
+                            pb[0] = gr(b_lo) | (gr(b2) << 16);
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < C; ++c) {
+                                // bytes c and C + c to the two halves
+                                const uint32_t sel = 0x0c000c00u | ((uint32_t)(C + c) << 16) | (uint32_t)c;
+                                pa[c] = __builtin_amdgcn_perm(a_hi, a_lo, sel);
+                                pb[c] = __builtin_amdgcn_perm(b_hi, b_lo, sel);
+                            }
+                        }
                     }
-                    // the second tap's C bytes, shifted down to byte 0
-                    const uint32_t a2 = tnext[p] ? __builtin_amdgcn_alignbyte(a_hi, a_lo, C % 4 == 0 ? 0 : C)
-                                                 : a_lo;
-                    const uint32_t b2 = tnext[p] ? __builtin_amdgcn_alignbyte(b_hi, b_lo, C % 4 == 0 ? 0 : C)
-                                                 : b_lo;
-                    const uint32_t a2w = (C == 4 && tnext[p]) ? a_hi : a2;
-                    const uint32_t b2w = (C == 4 && tnext[p]) ? b_hi : b2;
                     if constexpr (OUT == kOutGrey) {
-                        auto gr = [](uint32_t w) {
-                            return grey_u8(w & 255u, (w >> 8) & 255u, (w >> 16) & 255u);
-                        };
-                        resg[p] = (T)blend_u8(gr(a_lo), gr(a2w), gr(b_lo), gr(b2w), tw[p], wy1);
+                        fx[p] = blend_u8_pairs(pa[0], pb[0], twp[p], wy0x4, wy1x4);
                     } else {
 #pragma unroll
-                        for (int c = 0; c < C; ++c) {
-                            const unsigned p00 = (a_lo >> (8 * c)) & 255u, p01 = (a2w >> (8 * c)) & 255u;
-                            const unsigned p10 = (b_lo >> (8 * c)) & 255u, p11 = (b2w >> (8 * c)) & 255u;
-                            res[p * C + c] = (T)blend_u8(p00, p01, p10, p11, tw[p], wy1);
-                        }
+                        for (int c = 0; c < C; ++c)
+                            fx[p * C + c] = blend_u8_pairs(pa[c], pb[c], twp[p], wy0x4, wy1x4);
                     }
                 } else {
                     // float taps sit at 4-byte aligned LDS addresses (the
@@ -1752,6 +1799,16 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
                 }
             }
         }
+        if constexpr (U8LIN && OUT == kOutSame) {
+            uint32_t wds[PX * C / 4];
+#pragma unroll
+            for (int k = 0; k < PX * C / 4; ++k)
+                wds[k] = pack_byte3(fx[4 * k], fx[4 * k + 1], fx[4 * k + 2], fx[4 * k + 3]);
+            __builtin_memcpy(res, wds, sizeof(wds));
+        } else if constexpr (U8LIN && OUT == kOutGrey) {
+#pragma unroll
+            for (int p = 0; p < PX; ++p) resg[p] = (T)(fx[p] >> 24);
+        }
         if (valid_px > 0) {
             if constexpr (OUT == kOutSame && NSTAGE > 0) {
                 if (nstaged) {
@@ -1771,8 +1828,12 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             } else {
                 float f[PX * C];
 #pragma unroll
-                for (int k = 0; k < PX * C; ++k)
-                    f[k] = fmaf((float)res[k], aff.scale[k % C], aff.bias[k % C]);
+                for (int k = 0; k < PX * C; ++k) {
+                    float v;
+                    if constexpr (U8LIN) v = (float)(fx[k] >> 24);   // byte 3, converted directly
+                    else v = (float)res[k];
+                    f[k] = fmaf(v, aff.scale[k % C], aff.bias[k % C]);
+                }
                 float *dstf = (float *)dst_v;
                 if constexpr (OUT == kOutNormNHWC) {
                     if (nstaged) {
