@@ -129,8 +129,9 @@ def parse():
                    help="skip the informational warm-cache figure")
     p.add_argument("--streams", type=int, default=3,
                    help="HIP streams of the sustained measurement (default 3)")
-    p.add_argument("--ceiling", action="store_true",
-                   help="instead of resizing, run the launch / bandwidth ceiling program")
+    p.add_argument("--ceiling", nargs="*", default=None, metavar="SECTION",
+                   help="instead of resizing, run the launch / bandwidth ceiling program "
+                        "(all sections, or the ones named)")
     p.add_argument("--suite", action="store_true",
                    help="instead of one workload, measure every workload cold and warm and "
                         "time the oracle on each (single thread and all host cores)")
@@ -401,16 +402,17 @@ def cpu_single_thread(w, src_np, mode, budget_s):
             "sample": "%d whole %s frame(s), %.1f s, %.2f ms per frame" % (reps, w.name, el, per * 1e3)}
 
 
-def ceiling():
+def ceiling(sections=None):
     """Runs the ceiling program (copy throughput against size, empty-grid
     launch costs, a read-only stream, the 4K frame on 1-4 streams, a
-    per-wave trace of a stand-in for the 2:1 kernel) and passes its JSON
-    lines through."""
+    per-wave trace of a stand-in for the 2:1 kernel, the exact 2x kernel
+    beside stand-ins of its byte mix) and passes its JSON lines through;
+    `sections` names a subset."""
     import subprocess
     exe = os.path.join(ROOT, "bilinear_image_resize_amd", "mi_resize_ceiling")
     if not os.path.exists(exe):
         sys.exit("the ceiling program is not built: run __graft_entry__.build() first")
-    sys.exit(subprocess.call([exe]))
+    sys.exit(subprocess.call([exe] + list(sections or [])))
 
 
 def oracle_rate(w, src_np, mode, threads, budget_s):
@@ -531,8 +533,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args)
         return
-    if args.ceiling:
-        ceiling()
+    if args.ceiling is not None:
+        ceiling(args.ceiling)
     if args.suite:
         suite(args)
         return

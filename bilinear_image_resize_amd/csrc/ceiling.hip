@@ -4,9 +4,10 @@
 // library's own entry points (resize_linear, resize_copy_bytes) through the
 // C ABI - including the 4K RGB frame on 1 to 4 streams and the exact 2:1
 // kernel over a range of frame heights - plus a few kernels of its own that bound what any kernel of the
-// same shape can reach (an empty grid, a read-only stream, and a stand-in
+// same shape can reach (an empty grid, a read-only stream, a stand-in
 // with the exact 2:1 kernel's loads, stores and grid that records when each
-// workgroup starts and ends).  It prints one JSON object per line.
+// workgroup starts and ends, and stand-ins with the exact 2x kernel's grid
+// and byte mix).  It prints one JSON object per line.
 //
 // Timing follows the method of "From Prototype to Performance: Optimizing
 // OpenCV Resize on Volcanic GPUs" (section "Measure performance carefully":
@@ -16,13 +17,14 @@
 // are enqueued, so the events time launches that follow each other back to
 // back rather than the host's enqueue rate.
 //
-//     mi_resize_ceiling            (all sections)
+//     mi_resize_ceiling [section ...]    (all sections by default)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 #include <vector>
 
 #include "mi_resize.h"
@@ -124,6 +126,51 @@ __global__ __launch_bounds__(128) void traced_half_rgb(const uint8_t *__restrict
         tr[2 * item] = t0;
         tr[2 * item + 1] = wall_clock64();
     }
+}
+
+// Stand-ins for the exact 2x one-channel kernel on a 1080 x 1920 frame
+// (output 2160 x 3840) with its grid: four-wave workgroups over (512-pixel
+// segment, group of four row gaps), renumbered so that each XCD takes a
+// contiguous run, one wave per gap, each lane owning 8 source columns and so
+// 16 output bytes of each of the gap's two output rows.  Gap g (-1 .. 1079)
+// lies between source rows g and g + 1 and writes output rows 2g + 1 and
+// 2g + 2 where they exist.  READ = false writes without reading anything;
+// READ = true first loads, as the kernel does, a 16-byte window around the
+// lane's 8 bytes of both source rows (clamped into the frame) and writes
+// bytes made from them.  Together they bound what any kernel with this byte
+// mix and grid can reach.
+constexpr int kU2H = 1080, kU2W = 1920, kU2Segs = 4, kU2Gaps = kU2H + 1;
+constexpr int kU2GapGroups = (kU2Gaps + 3) / 4;
+
+__device__ __forceinline__ unsigned xcd_run(unsigned lin, unsigned nwg)
+{
+    const unsigned xcd = lin & 7;
+    return xcd * (nwg >> 3) + min(xcd, nwg & 7) + (lin >> 3);
+}
+
+template <bool READ>
+__global__ __launch_bounds__(256) void up2_standin(const uint8_t *__restrict__ src,
+                                                   uint8_t *__restrict__ dst)
+{
+    const unsigned wid = xcd_run(blockIdx.x, gridDim.x);
+    const int seg = (int)(wid % kU2Segs), grp = (int)(wid / kU2Segs);
+    const int gap = grp * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) - 1;
+    const int x0 = seg * 512 + 8 * ((int)threadIdx.x & 63);
+    if (gap >= kU2H || x0 >= kU2W) return;
+    u32x4 o = {(unsigned)gap, (unsigned)x0, 0x01010101u, 0x02020202u};
+    if (READ) {
+        const int ra = gap < 0 ? 0 : gap, rb = gap + 1 > kU2H - 1 ? kU2H - 1 : gap + 1;
+        const int xw = x0 < 4 ? 0 : (x0 + 12 > kU2W ? kU2W - 16 : x0 - 4);
+        u32x4 a, b;   // 4-byte aligned windows, as in the kernel
+        __builtin_memcpy(&a, __builtin_assume_aligned(src + (size_t)ra * kU2W + xw, 4), 16);
+        __builtin_memcpy(&b, __builtin_assume_aligned(src + (size_t)rb * kU2W + xw, 4), 16);
+        o = a ^ b.yzwx;
+    }
+    if (2 * gap + 1 >= 0)
+        __builtin_nontemporal_store(o, (u32x4 *)(dst + (size_t)(2 * gap + 1) * (2 * kU2W) + 2 * x0));
+    if (2 * gap + 2 <= 2 * kU2H - 1)
+        __builtin_nontemporal_store(o ^ 0x5a5a5a5au,
+                                    (u32x4 *)(dst + (size_t)(2 * gap + 2) * (2 * kU2W) + 2 * x0));
 }
 
 int g_wall_khz = 100000;
@@ -323,6 +370,52 @@ void resize_rows_fit(hipStream_t *st)
            31104000.0 / ((31104000.0 / (0.7 * kPeakGBps * 1e3) - icpt) * 1e3));
 }
 
+// The exact 2x one-channel resize (1080 x 1920 -> 2160 x 3840) beside the
+// stand-ins above and a copy of the same bytes split evenly between reads
+// and writes.
+void up2_byte_mix(hipStream_t *st)
+{
+    const long long sb = (long long)kU2H * kU2W, db = 4 * sb;
+    const int pairs = (int)(kRotateBytes / (sb + db)) + 1;
+    Ring srcs((size_t)sb, pairs), dsts((size_t)db, pairs);
+    const unsigned wgs = kU2Segs * kU2GapGroups;
+    auto report = [&](const char *what, double us, long long bytes) {
+        printf("{\"section\": \"up2x_byte_mix\", \"what\": \"%s\", \"bytes\": %lld, \"us\": %.3f, "
+               "\"GBps\": %.1f, \"frac_of_peak\": %.4f}\n",
+               what, bytes, us, bytes / (us * 1e3), bytes / (us * 1e3) / kPeakGBps);
+    };
+    auto wo = [&](int i, hipStream_t s) {
+        hipLaunchKernelGGL(up2_standin<false>, dim3(wgs), dim3(256), 0, s, srcs.p[i % pairs],
+                           dsts.p[i % pairs]);
+    };
+    report("stand-in, writes only (8.29 MB)", time_us(wo, 400, 1, st), db);
+    auto rw = [&](int i, hipStream_t s) {
+        hipLaunchKernelGGL(up2_standin<true>, dim3(wgs), dim3(256), 0, s, srcs.p[i % pairs],
+                           dsts.p[i % pairs]);
+    };
+    report("stand-in, both source rows read then written", time_us(rw, 400, 1, st), sb + db);
+    auto lin = [&](int i, hipStream_t s) {
+        if (resize_linear(srcs.p[i % pairs], dsts.p[i % pairs], 1, kU2H, kU2W, 1, MI_RESIZE_U8,
+                          2 * kU2H, 2 * kU2W, s) != 0)
+            exit(3);
+    };
+    report("resize_linear 2x", time_us(lin, 400, 1, st), sb + db);
+    auto nn = [&](int i, hipStream_t s) {
+        if (resize_nearest(srcs.p[i % pairs], dsts.p[i % pairs], 1, kU2H, kU2W, 1, MI_RESIZE_U8,
+                           2 * kU2H, 2 * kU2W, s) != 0)
+            exit(3);
+    };
+    report("resize_nearest 2x", time_us(nn, 400, 1, st), sb + db);
+    // the same-bytes copy: (sb + db) / 2 each way, from the destinations
+    // (each at least that large) into the sources' ring of the same count
+    const long long half = (sb + db) / 2;
+    Ring other((size_t)half, pairs);
+    auto cp = [&](int i, hipStream_t s) {
+        if (resize_copy_bytes(dsts.p[i % pairs], other.p[(i + 1) % pairs], half, s) != 0) exit(2);
+    };
+    report("copy of the same bytes, half read and half written", time_us(cp, 400, 1, st), sb + db);
+}
+
 void trace_4k(hipStream_t *st)
 {
     const long long sb = 24883200, db = 6220800;
@@ -371,24 +464,28 @@ void trace_4k(hipStream_t *st)
 
 }  // namespace
 
-int main()
+int main(int argc, char **argv)
 {
+    // optional arguments name the sections to run (all by default)
+    auto want = [&](const char *name) {
+        if (argc < 2) return true;
+        for (int i = 1; i < argc; ++i)
+            if (std::string(argv[i]) == name) return true;
+        return false;
+    };
     CK(hipDeviceGetAttribute(&g_wall_khz, hipDeviceAttributeWallClockRate, 0));
     hipStream_t st[4];
     for (auto &s : st) CK(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
-    fflush(stdout);
-    copy_vs_size(st);
-    fflush(stdout);
-    empty_grids(st);
-    fflush(stdout);
-    read_only_stream(st);
-    fflush(stdout);
-    resize_4k(st);
-    fflush(stdout);
-    resize_rows_fit(st);
-    fflush(stdout);
-    trace_4k(st);
-    fflush(stdout);
+    const struct { const char *name; void (*run)(hipStream_t *); } sections[] = {
+        {"copy_vs_size", copy_vs_size},   {"empty_grid", empty_grids},
+        {"read_only", read_only_stream},  {"resize_4k_rgb", resize_4k},
+        {"resize_rgb_2to1_rows", resize_rows_fit}, {"trace_4k_rgb_standin", trace_4k},
+        {"up2x_byte_mix", up2_byte_mix}};
+    for (const auto &sec : sections) {
+        if (!want(sec.name)) continue;
+        sec.run(st);
+        fflush(stdout);
+    }
     for (auto &s : st) CK(hipStreamDestroy(s));
     return 0;
 }

@@ -817,34 +817,61 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
     const bool left = m > 0, right = (m + 1) * S < W;
     // rows of two or more chunks hold IN + 8 bytes around every chunk
     const bool one_load = chunks_per_row >= 2;
-    // horizontal sums of one source row, one u16x2 per output byte pair
-    auto hsum = [&](const uint8_t *row, u16x2 (&h)[NP]) {
-        const uint8_t *p = row + (size_t)m * IN;      // 4-byte aligned
-        uint32_t e[ND];
+    // The lane's source windows of both rows, each a dword window around
+    // the lane's IN bytes with the edge pixel moved into a missing
+    // neighbour.  Both rows' loads issue before the first wait: loading and
+    // shifting each row in turn put the wait for row a's load, behind the
+    // uniform branch on the window's shape, before row b's load was issued
+    // (two memory round trips per wave).
+    // one_load: the whole window in one load per row, [p - 4, p + IN + 4)
+    // inside the row, [p, p + IN + 8) at its start and [p - 8, p + IN) at
+    // its end, then shifted into place (one 16-byte load per row for C = 1
+    // instead of three loads: 1080p grey 3.49 -> 3.42 us).  Otherwise a
+    // one-chunk row: its bytes and its own edge dwords.
+    auto windows = [&](const uint8_t *row_a, const uint8_t *row_b, uint32_t (&ea)[ND],
+                       uint32_t (&eb)[ND]) {
+        const uint8_t *pa = row_a + (size_t)m * IN, *pb = row_b + (size_t)m * IN;   // 4-byte aligned
         if (one_load) {
-            // the whole window in one load: [p - 4, p + IN + 4) inside the
-            // row, [p, p + IN + 8) at its start and [p - 8, p + IN) at its
-            // end, then shifted into place, with the edge pixel moved into
-            // the missing neighbour (one 16-byte load per row for C = 1
-            // instead of three loads: 1080p grey 3.49 -> 3.42 us)
             const int sh = !left ? 0 : (!right ? -8 : -4);
-            uint32_t L[ND];
-            __builtin_memcpy(L, __builtin_assume_aligned(p + sh, 4), 4 * ND);
+            uint32_t A[ND], B[ND];
+            __builtin_memcpy(A, __builtin_assume_aligned(pa + sh, 4), 4 * ND);
+            __builtin_memcpy(B, __builtin_assume_aligned(pb + sh, 4), 4 * ND);
 #pragma unroll
-            for (int k = 0; k < ND; ++k)
-                e[k] = !left ? L[k > 0 ? k - 1 : 0] : (!right ? L[k < ND - 1 ? k + 1 : ND - 1] : L[k]);
-            if (!left) e[0] = L[0] << (8 * (4 - C));
-            if (!right) e[ND - 1] = L[ND - 1] >> (8 * (4 - C));
+            for (int k = 0; k < ND; ++k) {
+                const uint32_t a_m = A[k > 0 ? k - 1 : 0], a_0 = A[k], a_p = A[k < ND - 1 ? k + 1 : ND - 1];
+                const uint32_t b_m = B[k > 0 ? k - 1 : 0], b_0 = B[k], b_p = B[k < ND - 1 ? k + 1 : ND - 1];
+                ea[k] = !left ? a_m : (!right ? a_p : a_0);
+                eb[k] = !left ? b_m : (!right ? b_p : b_0);
+            }
+            if (!left) {
+                ea[0] = A[0] << (8 * (4 - C));
+                eb[0] = B[0] << (8 * (4 - C));
+            }
+            if (!right) {
+                ea[ND - 1] = A[ND - 1] >> (8 * (4 - C));
+                eb[ND - 1] = B[ND - 1] >> (8 * (4 - C));
+            }
         } else {
-            __builtin_memcpy(&e[1], __builtin_assume_aligned(p, IN % 16 == 0 ? 16 : 8), IN);
-            // a one-chunk row: its own edge dwords with the edge pixels moved
-            // into place.  Both loads are unconditional so that all of them
-            // issue before the first wait.
-            const uint32_t lw = *(const uint32_t *)p;
-            const uint32_t rw = *(const uint32_t *)(p + IN - 4);
-            e[0] = lw << (8 * (4 - C));
-            e[ND - 1] = rw >> (8 * (4 - C));
+            uint32_t A[ND - 2], B[ND - 2];
+            __builtin_memcpy(A, __builtin_assume_aligned(pa, IN % 16 == 0 ? 16 : 8), IN);
+            __builtin_memcpy(B, __builtin_assume_aligned(pb, IN % 16 == 0 ? 16 : 8), IN);
+            // both loads unconditional, so that all of them issue before the first wait
+            const uint32_t lwa = *(const uint32_t *)pa, rwa = *(const uint32_t *)(pa + IN - 4);
+            const uint32_t lwb = *(const uint32_t *)pb, rwb = *(const uint32_t *)(pb + IN - 4);
+            // (element-wise: a memcpy into part of ea sent the windows to scratch)
+#pragma unroll
+            for (int k = 0; k < ND - 2; ++k) {
+                ea[k + 1] = A[k];
+                eb[k + 1] = B[k];
+            }
+            ea[0] = lwa << (8 * (4 - C));
+            ea[ND - 1] = rwa >> (8 * (4 - C));
+            eb[0] = lwb << (8 * (4 - C));
+            eb[ND - 1] = rwb >> (8 * (4 - C));
         }
+    };
+    // horizontal sums of one source row's window, one u16x2 per output byte pair
+    auto hsum = [&](const uint32_t (&e)[ND], u16x2 (&h)[NP]) {
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const u16x2 u = __builtin_bit_cast(u16x2, up2_pick<C, true, ND>(e, 2 * j));
@@ -871,9 +898,11 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
         const size_t off_b = ((size_t)n * 2 * H + (size_t)(2 * g + 2)) * (2 * row_bytes) +
                           (size_t)bx * 64 * OUT;
         if (active) {
+            uint32_t ea[ND], eb[ND];
+            windows(img + (size_t)ra * row_bytes, img + (size_t)rb * row_bytes, ea, eb);
             u16x2 ha[NP], hb[NP];
-            hsum(img + (size_t)ra * row_bytes, ha);
-            hsum(img + (size_t)rb * row_bytes, hb);
+            hsum(ea, ha);
+            hsum(eb, hb);
             uint32_t oa[OUT / 4], ob[OUT / 4];
 #pragma unroll
             for (int w = 0; w < OUT / 4; ++w) {
