@@ -1147,8 +1147,8 @@ __device__ __forceinline__ int seg_lane() { return (int)threadIdx.x & (kSegLanes
 // One source-row segment to stage: `bytes` bytes from p (uniform across the
 // wave) into an LDS slot, as 16-byte chunks from the 16-byte boundary at or
 // below p.  `clean` says every chunk lies wholly inside the source buffer
-// [lo, hi), which is the case for every row except possibly the buffer's
-// first and last ones.
+// [lo, hi); the caller decides it from the row (see rowseg), and segments
+// that are not clean are staged with every chunk checked.
 struct Segment {
     const uint8_t *base;   // 16-byte aligned address of chunk 0
     uint8_t *slot;
@@ -1156,15 +1156,13 @@ struct Segment {
     int n16;               // chunks to stage
     bool on;               // this row needs staging
     bool clean;
-    __device__ void plan(bool want, uint8_t *slot_, const uint8_t *p, int bytes,
-                         const uint8_t *lo, const uint8_t *hi)
+    __device__ void plan(bool want, uint8_t *slot_, const uint8_t *p, int bytes)
     {
         on = want;
         slot = slot_;
         mis = (int)((uintptr_t)p & 15);
         base = p - mis;
         n16 = (mis + bytes + 15) >> 4;
-        clean = base >= lo && base + 16 * (size_t)n16 <= hi;
     }
 };
 
@@ -1550,10 +1548,14 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
     const uint8_t *lo = (const uint8_t *)src;
     const uint8_t *hi = lo + (size_t)src_elems * sizeof(T);
     const size_t row_bytes = (size_t)W * PB;
+    const unsigned row_bytes32 = (unsigned)W * PB;   // below 2^20
+    const size_t img_bytes = (size_t)H * row_bytes;
     T *const out_lane = dst + (size_t)x0 * C;
 
-    // Planning state: the next output row to plan, its crop and segment.
+    // Planning state: the next output row to plan, its image's first source
+    // row, its crop and segment.
     long long pn = n0;
+    const uint8_t *pimg = lo + (size_t)n0 * img_bytes;
     int pdy = (int)(g - n0 * dH);
     int seg_sa;                      // first source column, relative to the crop
     int psa, pbytes;                 // first staged source column (absolute), bytes
@@ -1578,10 +1580,36 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         ys.init_biased(d, crop.h, dH, NEAREST ? nearest_bias(nn_map, crop.h, dH) : crop.h - dH);
     };
     row_init(pdy);
-    // global source row held in each LDS slot, and its offset there
-    long long held0 = -1, held1 = -1;
+    // source row (its first byte) held in each LDS slot, and its offset there
+    const uint8_t *held0 = nullptr, *held1 = nullptr;
     int mis0 = 0, mis1 = 0;
 
+    // Whether the 16-byte chunks of a segment of `row` (source rows lie
+    // row_bytes apart from lo) stay inside [lo, hi).  For rows of 16 bytes
+    // or more, a row after the first starts at least 16 bytes past lo, so a
+    // chunk there (at most 15 bytes before the segment) starts at or after
+    // lo; a row before the last ends at least 16 bytes before hi, so a chunk
+    // there (at most 15 bytes past the segment) ends at or before hi.  The
+    // first and last rows are checked exactly whenever the segment's columns
+    // change, and kept as lo_bad / last_bad where their chunks leave the
+    // buffer (null otherwise).  Narrower rows are always staged with checks.
+    const uint8_t *const last_row = hi - row_bytes;
+    const bool wide_rows = row_bytes >= 16;
+    const uint8_t *lo_bad = nullptr, *last_bad = nullptr;
+    auto edge_rows = [&]() {
+        auto leaves = [&](const uint8_t *row) {
+            const uint8_t *p = row + (size_t)psa * PB;
+            const int mis = (int)((uintptr_t)p & 15);
+            const uint8_t *b = p - mis;
+            return b < lo || b + 16 * (size_t)((mis + pbytes + 15) >> 4) > hi;
+        };
+        lo_bad = leaves(lo) ? lo : nullptr;
+        last_bad = leaves(last_row) ? last_row : nullptr;
+    };
+    edge_rows();
+    auto chunks_inside = [&](const uint8_t *row) {
+        return wide_rows && row != lo_bad && row != last_bad;
+    };
     // Choose the source rows, weights and LDS slots of the planned row; the
     // slots are claimed now, their contents land at the next commit.
     auto plan_row = [&](RowPlan &P) {
@@ -1612,7 +1640,9 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
             if constexpr (sizeof(T) == 1) P.wy1 = weight11(t);
             else P.wyf = weightf(t);
         }
-        const long long ra = pn * H + crop.y + ya, rb = pn * H + crop.y + yb;
+        // rows within the image: one 32 x 32 -> 64-bit product each
+        const uint8_t *ra = pimg + (size_t)((unsigned)(crop.y + ya)) * row_bytes32;
+        const uint8_t *rb = pimg + (size_t)((unsigned)(crop.y + yb)) * row_bytes32;
         int sa_slot = held0 == ra ? 0 : (held1 == ra ? 1 : -1);
         int sb_slot = held0 == rb ? 0 : (held1 == rb ? 1 : -1);
         const bool need_a = sa_slot < 0;
@@ -1620,13 +1650,13 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         if (rb == ra) sb_slot = sa_slot;
         const bool need_b = sb_slot < 0;
         if (need_b) sb_slot = 1 - sa_slot;
-        P.A.plan(need_a, lds + sa_slot * slot_bytes + PAD,
-                 lo + (size_t)ra * row_bytes + (size_t)psa * PB, pbytes, lo, hi);
-        P.B.plan(need_b, lds + sb_slot * slot_bytes + PAD,
-                 lo + (size_t)rb * row_bytes + (size_t)psa * PB, pbytes, lo, hi);
+        P.A.plan(need_a, lds + sa_slot * slot_bytes + PAD, ra + (size_t)psa * PB, pbytes);
+        P.B.plan(need_b, lds + sb_slot * slot_bytes + PAD, rb + (size_t)psa * PB, pbytes);
+        P.A.clean = chunks_inside(ra);
+        P.B.clean = chunks_inside(rb);
         if constexpr (B == kBorderWrap) {
-            P.row_a = lo + (size_t)ra * row_bytes;
-            P.row_b = lo + (size_t)rb * row_bytes;
+            P.row_a = ra;
+            P.row_b = rb;
         }
         if (need_a) {
             if (sa_slot == 0) { held0 = ra; mis0 = P.A.mis; } else { held1 = ra; mis1 = P.A.mis; }
@@ -1646,9 +1676,11 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         if (++pdy == dH) {
             pdy = 0;
             ++pn;
+            pimg += img_bytes;
             if constexpr (ROI) {
                 crop = load_crop(rois, pn, H, W);
                 set_segment();
+                edge_rows();
             }
             row_init(0);
         } else {
