@@ -714,7 +714,11 @@ def test_grey_random_shapes(dtype, path, monkeypatch):
         N, H, W, C, dH, dW = random_case(r)
         shapes.append((N, H, W, 3 + (C == 4), dH, dW))
     shapes += [(1, 1, 1, 3, 1, 1), (1, 1, 7, 4, 5, 1), (2, 33, 65, 3, 17, 129), (1, 600, 600, 4, 2, 3),
-               (2, 64, 128, 3, 32, 64), (1, 48, 96, 4, 24, 48), (3, 20, 1040, 3, 10, 520)]   # exact 2:1
+               (2, 64, 128, 3, 32, 64), (1, 48, 96, 4, 24, 48), (3, 20, 1040, 3, 10, 520),   # exact 2:1
+               # row enlargements in batches: source rows repeat within an
+               # image, never across an image boundary
+               (3, 17, 230, 3, 40, 310), (2, 30, 500, 4, 45, 700), (4, 9, 300, 3, 25, 280),
+               (2, 40, 600, 3, 50, 400)]
     for i, (N, H, W, C, dH, dW) in enumerate(shapes):
         say("case grey %s %s #%d %s" % (dtype, path, i, (N, H, W, C, dH, dW)))
         s = random_image(r, (N, H, W, C), dtype)
