@@ -792,6 +792,56 @@ __device__ __forceinline__ uint32_t up2_pick(const uint32_t (&e)[ND], int k)
     return __builtin_amdgcn_perm(e[d + 1], e[d], up2_pair_sel(a, b, d));
 }
 
+// One-channel rows on 4-byte dot products.  Output byte q of row 2g + 1
+// or 2g + 2 is (9 t + 3 u + 3 v + w + 8) >> 4 over its four taps (the near
+// and far column of the near and far row), the same sum as the packed form
+// above; scaled by 16, with 128 added, it is below 2^16 and its byte 1 is
+// the result.  Source pixels i and i + 1 (window bytes 4 + i, 5 + i) give
+// one register (a_i, a_i+1, b_i, b_i+1) - one byte permute, or three where
+// the pair straddles a dword - that serves output bytes 2i + 1 (i weighted
+// 3, i + 1 weighted 1) and 2i + 2 (the other way round) of both rows: four
+// weight vectors, 16 x (vertical x horizontal) weights on those bytes.
+// Checked bit for bit against the oracle on the CPU before its first run.
+template <int S, int ND>
+__device__ __forceinline__ void up2_rows_c1(const uint32_t (&ea)[ND], const uint32_t (&eb)[ND],
+                                            uint32_t (&oa)[S / 2], uint32_t (&ob)[S / 2])
+{
+    static_assert(ND == S / 4 + 2, "window of the lane's bytes and a dword each side");
+    constexpr uint32_t kOddA = 0x10303090u, kOddB = 0x30901030u;    // q = 2i + 1
+    constexpr uint32_t kEvenA = 0x30109030u, kEvenB = 0x90303010u;  // q = 2i + 2
+    uint32_t G[S + 1];   // G[j]: source pixels j - 1 and j (window bytes 3 + j, 4 + j)
+#pragma unroll
+    for (int j = 0; j <= S; ++j) {
+        const int lo = 3 + j, d = lo / 4, o = lo % 4;
+        if (o != 3) {
+            const uint32_t sel = (uint32_t)o | ((uint32_t)(o + 1) << 8) | ((uint32_t)(4 + o) << 16) |
+                                 ((uint32_t)(5 + o) << 24);
+            G[j] = __builtin_amdgcn_perm(eb[d], ea[d], sel);
+        } else {
+            const uint32_t sa = __builtin_amdgcn_alignbyte(ea[d + 1], ea[d], 3);
+            const uint32_t sb = __builtin_amdgcn_alignbyte(eb[d + 1], eb[d], 3);
+            G[j] = __builtin_amdgcn_perm(sb, sa, 0x05040100u);
+        }
+    }
+    uint32_t ra[2 * S], rb[2 * S];
+#pragma unroll
+    for (int q = 0; q < 2 * S; ++q) {
+        const int j = (q + 1) / 2;
+        ra[q] = __builtin_amdgcn_udot4(G[j], q % 2 ? kOddA : kEvenA, 128u, false);
+        rb[q] = __builtin_amdgcn_udot4(G[j], q % 2 ? kOddB : kEvenB, 128u, false);
+    }
+    // byte 1 of four results per output dword
+#pragma unroll
+    for (int w = 0; w < S / 2; ++w) {
+        oa[w] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ra[4 * w + 3], ra[4 * w + 2], 0x0c0c0501u),
+                                      __builtin_amdgcn_perm(ra[4 * w + 1], ra[4 * w], 0x0c0c0501u),
+                                      0x05040100u);
+        ob[w] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(rb[4 * w + 3], rb[4 * w + 2], 0x0c0c0501u),
+                                      __builtin_amdgcn_perm(rb[4 * w + 1], rb[4 * w], 0x0c0c0501u),
+                                      0x05040100u);
+    }
+}
+
 template <int C, int RB, bool ONE = false>
 __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W,
@@ -910,14 +960,18 @@ __global__ __launch_bounds__(64 * RB) void linear_up2_u8(
         if (active) {
             uint32_t ea[ND], eb[ND];
             windows(img + (size_t)ra * row_bytes, img + (size_t)rb * row_bytes, ea, eb);
-            u16x2 ha[NP], hb[NP];
-            hsum(ea, ha);
-            hsum(eb, hb);
             uint32_t oa[OUT / 4], ob[OUT / 4];
+            if constexpr (C == 1) {
+                up2_rows_c1<S, ND>(ea, eb, oa, ob);
+            } else {
+                u16x2 ha[NP], hb[NP];
+                hsum(ea, ha);
+                hsum(eb, hb);
 #pragma unroll
-            for (int w = 0; w < OUT / 4; ++w) {
-                oa[w] = vsum(ha, hb, w);      // row 2g + 1: 3 x row g + row g + 1
-                ob[w] = vsum(hb, ha, w);      // row 2g + 2: row g + 3 x row g + 1
+                for (int w = 0; w < OUT / 4; ++w) {
+                    oa[w] = vsum(ha, hb, w);      // row 2g + 1: 3 x row g + row g + 1
+                    ob[w] = vsum(hb, ha, w);      // row 2g + 2: row g + 3 x row g + 1
+                }
             }
 #pragma unroll
             for (int k = 0; k < OUT / 16; ++k) {
