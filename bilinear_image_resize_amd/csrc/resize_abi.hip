@@ -218,10 +218,21 @@ constexpr long long kSegMinBandRowsRoi = 4;
 constexpr long long kSegTargetBandsUp = 5000;
 constexpr long long kSegMinBandRowsUp = 3;
 constexpr long long kSegMaxBandRowsUp = 6;
-// Below this many output pixels the launch is latency-bound and the direct
-// kernels (no staging round trip, no per-lane column table of PX entries)
-// finish first.
-constexpr long long kSmallOutPixels = 1LL << 16;
+// Below 2^19 output pixels from at most 2^20 source pixels the launch is
+// latency-bound and the direct kernels (no staging round trip, no per-lane
+// column table of PX entries, one row per workgroup) finish first:
+// 4 x 100x100 RGB -> 150x150 6.0 -> 3.4 us, 1x240x320 grey -> 400x530
+// 5.5 -> 3.7, 32 x 128x128 RGBA -> 100x100 6.2 -> 5.4.  Larger outputs
+// stay on the row-segment kernel (720x960 from 480x640 RGB 5.8 us there,
+// 6.6 direct), and so do downscales of large sources, which its staged rows
+// serve better (1080p RGB -> 540x800 6.6 vs 6.8).
+constexpr long long kSmallOutPixels = 1LL << 19;
+constexpr long long kSmallSrcPixels = 1LL << 20;
+
+bool small_launch(int batch, int H, int W, int dH, int dW)
+{
+    return (long long)batch * dH * dW < kSmallOutPixels && (long long)batch * H * W < kSmallSrcPixels;
+}
 
 // Float RGB / RGBA enlarged along rows of the output (dW > W), linear or
 // nearest: every output pixel is 12 or 16 bytes, the output outweighs the
@@ -263,6 +274,11 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, long lo
         if (rpb < up) rpb = up;
     }
     if (rpb < min_rows) rpb = min_rows;
+    // but keep at least ~1024 bands (one wave per SIMD) where the rows
+    // allow: few rows in long bands leave most of the chip idle while each
+    // wave walks its rows (8 x 224x224 -> 256x256 RGB 5.8 -> 5.0 us)
+    const long long par = rows * gx / 1024;
+    if (rpb > par) rpb = par < 1 ? 1 : par;
     pl.rows_per_block = (int)rpb;
     const long long bands = (rows + rpb - 1) / rpb;
     pl.grid = dim3((unsigned)gx, (unsigned)((bands + kSegWaves - 1) / kSegWaves));
@@ -532,7 +548,7 @@ int linear_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
             return launch_up2_u8<C, false>(src, dst, batch, H, W, st);
     }
     int rc;
-    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    const bool small = small_launch(batch, H, W, dH, dW);
     if (path == Path::RowSeg ||
         (path == Path::Auto && !small && !prefer_direct<T, C>(W, dW)))
         if (try_rowseg<T, C, false>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
@@ -551,7 +567,7 @@ int nearest_dispatch(const void *src, void *dst, int batch, int H, int W, int dH
             return launch_up2_u8<C, true>(src, dst, batch, H, W, st);
     }
     int rc;
-    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    const bool small = small_launch(batch, H, W, dH, dW);
     // float RGB / RGBA enlargements: the direct kernel, as for linear
     // (1080p RGBA 2x 26.4 vs 41.8 us, RGB 2x 23.0 vs 87.1 us)
     if (path == Path::RowSeg ||
@@ -567,7 +583,7 @@ int normalize_dispatch(const void *src, float *dst, int batch, int H, int W, int
 {
     const Path path = path_override();
     int rc;
-    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    const bool small = small_launch(batch, H, W, dH, dW);
     if (path == Path::RowSeg || (path == Path::Auto && !small))
         if (try_rowseg<uint8_t, C, false, OUT>(src, dst, batch, H, W, dH, dW, st, rc, aff))
             return rc;
@@ -580,7 +596,7 @@ int roi_dispatch(const void *src, void *dst, int batch, int H, int W, const int3
 {
     const Path path = path_override();
     int rc;
-    const bool small = (long long)batch * dH * dW < kSmallOutPixels;
+    const bool small = small_launch(batch, H, W, dH, dW);
     if (path == Path::RowSeg || (path == Path::Auto && !small))
         if (try_rowseg<T, C, false, kOutSame, true>(src, dst, batch, H, W, dH, dW, st, rc,
                                                      Affine{}, rois))
@@ -595,7 +611,7 @@ int border_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
 {
     const long long rows = (long long)batch * dH;
     const Path path = path_override();
-    const bool small = rows * dW < kSmallOutPixels;
+    const bool small = small_launch(batch, H, W, dH, dW);
     if (path == Path::RowSeg ||
         (path == Path::Auto && !small && !prefer_direct<T, C>(W, dW))) {
         int rc;
@@ -633,7 +649,7 @@ int grey_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, i
         if (path == Path::Auto && half_path_fits(C, H, W, dH, dW, src, dst))
             return launch_half_u8<C, true>(src, dst, batch, dH, dW, st);
     }
-    const bool small = rows * dW < kSmallOutPixels;
+    const bool small = small_launch(batch, H, W, dH, dW);
     int rc;
     if (path == Path::RowSeg || (path == Path::Auto && !small))
         if (try_rowseg<T, C, false, kOutGrey>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
