@@ -274,10 +274,12 @@ bool plan_rowseg(int px, int pixel_bytes, int W, int dW, long long rows, long lo
         if (rpb < up) rpb = up;
     }
     if (rpb < min_rows) rpb = min_rows;
-    // but keep at least ~1024 bands (one wave per SIMD) where the rows
+    // but keep at least ~2048 bands (two waves per SIMD) where the rows
     // allow: few rows in long bands leave most of the chip idle while each
-    // wave walks its rows (8 x 224x224 -> 256x256 RGB 5.8 -> 5.0 us)
-    const long long par = rows * gx / 1024;
+    // wave walks its rows (8 x 224x224 -> 256x256 RGB 5.9 -> 4.8 us,
+    // 1080p RGB -> 540x800 6.6 -> 6.1; a 4096-band floor lost elsewhere,
+    // 4K RGB -> 1440x2560 11.9 -> 14.6)
+    const long long par = rows * gx / 2048;
     if (rpb > par) rpb = par < 1 ? 1 : par;
     pl.rows_per_block = (int)rpb;
     const long long bands = (rows + rpb - 1) / rpb;
