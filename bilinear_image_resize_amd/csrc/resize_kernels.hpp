@@ -75,13 +75,45 @@ __device__ __forceinline__ unsigned xcd_contiguous(unsigned lin, unsigned nwg)
 }
 
 // --------------------------------------------------------------------------
+// Exact floor division for the coordinate maps below: q = floor(num / den)
+// and r = num - q den in [0, den), for an integer num with |num / den| below
+// 2^17 and den in [1, 2^17).  The caller passes num twice: numf, num rounded
+// once to fp32 (an fma of exact small factors, or a correctly rounded
+// conversion), and num_lo, its low 32 bits.  The estimate numf x rcp(den)
+// carries three roundings of at most 2^-24, 2^-23 (the hardware reciprocal's
+// one ulp) and 2^-24 relative, so it lies within 2^17 x 2^-22 = 2^-5 of
+// num / den and its floor is q or q +- 1.  The remainder of that guess lies
+// in [-den, 2 den), inside 32 bits, so the wrapped 32-bit difference is
+// exact and one step in either direction fixes q.  About 8 instructions
+// where an fp64 division with its conversions costs ~40; checked against
+// integer floor division over the maps' full ranges (2 n_out, n_in up to
+// 65535, the biases used here, and reciprocals one ulp off either way).
+// --------------------------------------------------------------------------
+struct QR { int q, r; };
+
+__device__ __forceinline__ QR floor_divmod(float numf, unsigned num_lo, int den)
+{
+    int q = (int)floorf(numf * __builtin_amdgcn_rcpf((float)den));
+    int r = (int)(num_lo - (unsigned)__mul24(q, den));
+    if (r < 0) { q -= 1; r += den; } else if (r >= den) { q += 1; r -= den; }
+    return {q, r};
+}
+
+// floor_divmod of 2 d n_in + bias: every factor and the bias are below 2^24,
+// so one fma rounds the numerator once and 24-bit multiplies give its low
+// word (d < 2^16, n_in <= 65535, |bias| < 2^17).
+__device__ __forceinline__ QR map_divmod(int d2, int n_in, int bias, int den)
+{
+    return floor_divmod(__builtin_fmaf((float)d2, (float)n_in, (float)bias),
+                        __umul24((unsigned)d2, (unsigned)n_in) + (unsigned)bias, den);
+}
+
+// --------------------------------------------------------------------------
 // Coordinate map for one axis.  Output index d of an axis of n_out samples
 // taken from n_in samples: x = (d + 1/2) n_in / n_out - 1/2 = num / den with
 // num = (2d + 1) n_in - n_out, den = 2 n_out.  x0 = floor(x) and the
-// remainder r = num - x0 den in [0, den) are exact: num < 2^34 is exact in
-// double, the quotient is below 2^16, so its rounding error (< 2^-36) is far
-// smaller than the gap 1/den >= 2^-17 to the next integer, and the fix-up
-// below only guards the argument.  Taps are clamped to the edge.
+// remainder r = num - x0 den in [0, den) come out exact from floor_divmod
+// (the quotient lies in [-1, n_in)).  Taps are clamped to the edge.
 // --------------------------------------------------------------------------
 struct Tap {
     int a;      // clamp(x0, 0, n_in - 1)
@@ -92,16 +124,12 @@ struct Tap {
 
 __device__ __forceinline__ Tap axis_tap(int d, int n_in, int n_out)
 {
-    const long long num = (long long)(2 * d + 1) * n_in - n_out;
     const int den = 2 * n_out;
-    long long q = (long long)floor((double)num / (double)den);
-    long long r = num - q * den;
-    if (r < 0) { q -= 1; r += den; }
-    else if (r >= den) { q += 1; r -= den; }
+    const QR m = map_divmod(2 * d + 1, n_in, -n_out, den);
     Tap t;
-    t.a = (int)(q < 0 ? 0 : (q > n_in - 1 ? n_in - 1 : q));
-    t.b = (int)(q + 1 < 0 ? 0 : (q + 1 > n_in - 1 ? n_in - 1 : q + 1));
-    t.r = (int)r;
+    t.a = m.q < 0 ? 0 : (m.q > n_in - 1 ? n_in - 1 : m.q);
+    t.b = m.q + 1 < 0 ? 0 : (m.q + 1 > n_in - 1 ? n_in - 1 : m.q + 1);
+    t.r = m.r;
     t.den = den;
     return t;
 }
@@ -139,12 +167,11 @@ __device__ __forceinline__ Tap axis_tap_b(int d, int n_in, int n_out)
             if (num < 0) num += (long long)n_in * den;
             if (num >= (long long)n_in * den) num -= (long long)n_in * den;
         }
-        long long q = (long long)floor((double)num / (double)den);
-        long long r = num - q * den;
-        if (r < 0) { q -= 1; r += den; } else if (r >= den) { q += 1; r -= den; }
-        t.a = (int)q;
-        t.b = (int)(q + 1 < n_in ? q + 1 : (B == kBorderWrap ? 0 : n_in - 1));
-        t.r = (int)r;
+        // num now lies in [0, n_in den): the quotient in [0, n_in)
+        const QR m = floor_divmod((float)num, (unsigned)num, den);
+        t.a = m.q;
+        t.b = m.q + 1 < n_in ? m.q + 1 : (B == kBorderWrap ? 0 : n_in - 1);
+        t.r = m.r;
         return t;
     }
 }
@@ -194,13 +221,8 @@ __device__ __forceinline__ int nearest_bias(int map, int n_in, int n_out)
 
 __device__ __forceinline__ int nearest_index(int d, int n_in, int n_out, int map)
 {
-    const long long num = 2LL * d * n_in + nearest_bias(map, n_in, n_out);
-    const long long den = 2LL * n_out;
-    long long q = (long long)floor((double)num / (double)den);
-    long long r = num - q * den;
-    if (r < 0) q -= 1;
-    else if (r >= den) q += 1;
-    return (int)(q > n_in - 1 ? n_in - 1 : q);
+    const int q = map_divmod(2 * d, n_in, nearest_bias(map, n_in, n_out), 2 * n_out).q;
+    return q > n_in - 1 ? n_in - 1 : q;
 }
 
 // 11-bit fixed-point blend of one channel, exact in 32 bits:
@@ -1372,14 +1394,12 @@ struct AxisStepper {
     __device__ void init_biased(int d, int n_in, int n_out, int bias)
     {
         den = 2 * n_out;
-        const long long num = 2LL * d * n_in + bias;
-        long long q64 = (long long)floor((double)num / (double)den);
-        long long r64 = num - q64 * den;
-        if (r64 < 0) { q64 -= 1; r64 += den; } else if (r64 >= den) { q64 += 1; r64 -= den; }
-        q = (int)q64;
-        r = (int)r64;
-        dq = (2 * n_in) / den;
-        dr = 2 * n_in - dq * den;
+        const QR m = map_divmod(2 * d, n_in, bias, den);
+        q = m.q;
+        r = m.r;
+        const QR s = floor_divmod((float)(2 * n_in), (unsigned)(2 * n_in), den);
+        dq = s.q;
+        dr = s.r;
     }
     __device__ void next()
     {
