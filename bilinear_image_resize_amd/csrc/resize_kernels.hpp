@@ -260,11 +260,22 @@ __device__ __forceinline__ uint32_t row_sum_u8(uint32_t pair, uint32_t wx)
                                   0u, false);
 }
 
+// a * b + c on the full-rate 24-bit multiply-add: a and b below 2^24, the
+// result modulo 2^32.  Written out because from the plain expression the
+// compiler keeps two multiplies and a three-way add, one more instruction
+// per sum.
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c)
+{
+    uint32_t r;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // The vertical step: the rounded result in bits 24..31.
 __device__ __forceinline__ uint32_t col_sum_u8(uint32_t top, uint32_t bot, uint32_t wy0x4,
                                                uint32_t wy1x4)
 {
-    return __umul24(wy0x4, top) + __umul24(wy1x4, bot) + (1u << 23);
+    return mad_u24(wy0x4, top, mad_u24(wy1x4, bot, 1u << 23));
 }
 
 __device__ __forceinline__ uint32_t blend_u8_pairs(uint32_t pa, uint32_t pb, uint32_t wx,
