@@ -56,24 +56,24 @@ INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 MEASURED_TRAFFIC = {
     ("4k", "linear"): {"kernel": "linear_half_u8<3, false, false>",
                        "profile": "profiles/pmc_traffic_all_workloads.md",
-                       "kernel_source_sha256_16": "c1abe57934b72d0e",
-                       "fetch_kib": 12176.533, "write_kib": 6075.0,
-                       "fetch_scale": 1.99833, "write_scale": 0.99871},
+                       "kernel_source_sha256_16": "c87a6ea7a1e53cd8",
+                       "fetch_kib": 12176.518, "write_kib": 6075.0,
+                       "fetch_scale": 1.99833, "write_scale": 0.99904},
     ("up2x", "linear"): {"kernel": "linear_up2_u8<1, 4, true>",
                          "profile": "profiles/pmc_traffic_all_workloads.md",
-                         "kernel_source_sha256_16": "c1abe57934b72d0e",
-                         "fetch_kib": 1040.603, "write_kib": 8100.0,
-                         "fetch_scale": 1.99833, "write_scale": 0.99871},
+                         "kernel_source_sha256_16": "c87a6ea7a1e53cd8",
+                         "fetch_kib": 1040.598, "write_kib": 8100.0,
+                         "fetch_scale": 1.99833, "write_scale": 0.99904},
     ("thumb", "linear"): {"kernel": "rowseg<unsigned char, 3, false, 2, true, 0, false, 0, 0>",
                           "profile": "profiles/pmc_traffic_all_workloads.md",
-                          "kernel_source_sha256_16": "c1abe57934b72d0e",
-                          "fetch_kib": 107583.533, "write_kib": 38769.393,
-                          "fetch_scale": 1.99833, "write_scale": 0.99871},
+                          "kernel_source_sha256_16": "c87a6ea7a1e53cd8",
+                          "fetch_kib": 107575.511, "write_kib": 38580.008,
+                          "fetch_scale": 1.99833, "write_scale": 0.99904},
     ("rgbaf", "linear"): {"kernel": "rowseg<float, 4, false, 4, false, 0, false, 0, 0>",
                           "profile": "profiles/pmc_traffic_all_workloads.md",
-                          "kernel_source_sha256_16": "c1abe57934b72d0e",
-                          "fetch_kib": 318375.247, "write_kib": 296627.09,
-                          "fetch_scale": 1.99856, "write_scale": 0.99871},
+                          "kernel_source_sha256_16": "c87a6ea7a1e53cd8",
+                          "fetch_kib": 321911.123, "write_kib": 296627.093,
+                          "fetch_scale": 1.99857, "write_scale": 0.99904},
 }
 
 

@@ -1810,8 +1810,8 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
         ha = halo_load(P.A, P.row_a);
         hb = halo_load(P.B, P.row_b);
     }
-    // the lanes' column table (fp64 per lane) is built while the band's
-    // first rows load: nothing before the first commit reads it
+    // the lanes' column table (one division per lane) is built while the
+    // band's first rows load: nothing before the first commit reads it
     if constexpr (LDS_TABLE) {
 #pragma unroll
         for (int p = 0; p < PX; ++p) {
