@@ -288,6 +288,9 @@ EDGE = [
     # the widest rows of the exact 2x and 2:1 kernels (uint8) and of the
     # float RGB rows staged through LDS on the direct kernels
     (1, 2, 32760, 1, 4, 65520), (1, 4, 65504, 3, 2, 32752), (1, 2, 20000, 3, 3, 65532),
+    # coprime near-maximum lengths: coordinate quotients near 2^16 over
+    # denominators near 2^17, where the division's estimate is least precise
+    (1, 2, 65521, 3, 3, 65519), (1, 65519, 2, 1, 65521, 3),
 ]
 
 
