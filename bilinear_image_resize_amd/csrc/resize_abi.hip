@@ -70,19 +70,31 @@ int check_args(const void *src, const void *dst, int batch, int H, int W, int C,
 struct Grid {
     unsigned blocks;
     int rows_per_block;
-    int col_blocks;
+    BandGrid bg;
 };
 
-// Row-band grid shared by the generic kernels.
-Grid band_grid(long long rows_total, int dW)
+// m and s of FastDiv for a divisor d in [1, 2^31]
+FastDiv fast_div_for(long long d)
+{
+    unsigned s = 0;
+    while ((1LL << s) < d) ++s;
+    const unsigned long long m = ((1ULL << (31 + s)) + (unsigned long long)d - 1) / (unsigned long long)d;
+    return FastDiv{(unsigned)m, s};
+}
+
+// Row-band grid shared by the generic kernels (about kTargetBlocks
+// workgroups, so every workgroup index stays far below 2^31).
+Grid band_grid(long long rows_total, int dW, int dH)
 {
     Grid g;
-    g.col_blocks = (dW + kBlock - 1) / kBlock;
-    long long per_row = g.col_blocks;
+    g.bg.col_blocks = (dW + kBlock - 1) / kBlock;
+    long long per_row = g.bg.col_blocks;
     long long rpb = (rows_total * per_row + kTargetBlocks - 1) / kTargetBlocks;
     if (rpb < 1) rpb = 1;
     g.rows_per_block = (int)rpb;
     g.blocks = (unsigned)(((rows_total + rpb - 1) / rpb) * per_row);
+    g.bg.by_cols = fast_div_for(g.bg.col_blocks);
+    g.bg.by_dst_h = fast_div_for(dH);
     return g;
 }
 
@@ -112,12 +124,12 @@ int launch_linear_generic(const void *src, void *dst, int batch, int H, int W, i
                           const int32_t *rois = nullptr)
 {
     const long long rows = (long long)batch * dH;
-    const Grid g = band_grid(rows, dW);
+    const Grid g = band_grid(rows, dW, dH);
     const bool pix4 = OUT == kOutSame && C == 4 && aligned(src, 4 * sizeof(T)) &&
                       aligned(dst, 4 * sizeof(T));
     auto go = [&](auto kernel) {
         return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W, dH,
-                      dW, rows, g.rows_per_block, g.col_blocks, aff, rois);
+                      dW, rows, g.rows_per_block, g.bg, aff, rois);
     };
     if (pix4) return go(linear_generic<T, C, C == 4 && OUT == kOutSame, OUT, ROI>);
     if constexpr (sizeof(T) == 4 && C == 3 && OUT == kOutSame && !ROI) {
@@ -525,10 +537,10 @@ int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, 
                    int map, hipStream_t st)
 {
     const long long rows = (long long)batch * dH;
-    const Grid g = band_grid(rows, dW);
+    const Grid g = band_grid(rows, dW, dH);
     auto go = [&](auto kernel) {
         return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const uint8_t *)src,
-                      (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks, map);
+                      (uint8_t *)dst, H, W, dH, dW, rows, g.rows_per_block, g.bg, map);
     };
     if constexpr (BPP % 16 == 0) {
         if (aligned(src, 16) && aligned(dst, 16)) return go(nearest_generic<BPP, 16>);
@@ -633,11 +645,11 @@ int border_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
             return rc;
         }
     }
-    const Grid g = band_grid(rows, dW);
+    const Grid g = band_grid(rows, dW, dH);
     const bool pix4 = C == 4 && aligned(src, 4 * sizeof(T)) && aligned(dst, 4 * sizeof(T));
     auto go = [&](auto kernel) {
         return launch(kernel, dim3(g.blocks), dim3(kBlock), 0, st, (const T *)src, dst, H, W, dH,
-                      dW, rows, g.rows_per_block, g.col_blocks, Affine{},
+                      dW, rows, g.rows_per_block, g.bg, Affine{},
                       (const int32_t *)nullptr);
     };
     if (border == MI_RESIZE_BORDER_MIRROR) {
@@ -662,9 +674,9 @@ int grey_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, i
     int rc;
     if (path == Path::RowSeg || (path == Path::Auto && !small))
         if (try_rowseg<T, C, false, kOutGrey>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
-    const Grid g = band_grid(rows, dW);
+    const Grid g = band_grid(rows, dW, dH);
     return launch(linear_generic<T, C, false, kOutGrey>, dim3(g.blocks), dim3(kBlock), 0, st,
-                  (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block, g.col_blocks,
+                  (const T *)src, dst, H, W, dH, dW, rows, g.rows_per_block, g.bg,
                   Affine{}, (const int32_t *)nullptr);
 }
 
