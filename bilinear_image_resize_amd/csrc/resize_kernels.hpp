@@ -2144,6 +2144,178 @@ __global__ __launch_bounds__(kSegLanes * kSegWaves) void rowseg(
 }
 
 // --------------------------------------------------------------------------
+// Row enlargements of uint8 images by 2-D tiles (linear, clamp, plain output).
+//
+// A workgroup takes TH consecutive output rows of one image and the 64 PX
+// output columns of one segment.  Every source row those rows touch - at
+// most (TH - 1) H / dH + 3 of them, since the row step is below one - is
+// staged over the segment's source columns into LDS at once, so all of the
+// tile's 16-byte loads are in flight together; after one barrier the four
+// waves blend TH / 4 rows each from LDS.  The row-segment kernel walks a
+// band with one row of loads in flight, and an enlargement leaves each of
+// its waves so few rows that the chain of round trips per band, not
+// bandwidth or instruction issue, sets the time there.
+//
+// The column table (tap a's byte offset from column sa << 13, the
+// next-column flag << 12, the 11-bit weight) is built into LDS by all
+// threads, as in rowseg, and the blend is blend_u8_pairs: the results are
+// those of every other kernel, bit for bit.
+// --------------------------------------------------------------------------
+constexpr int kTileWaves = 4;
+
+// The launch's tile geometry (host-computed).
+struct TileGeom {
+    int tiles_x;           // column segments of 64 PX output columns per row
+    int tiles_y;           // row tiles of TH output rows per image
+    FastDiv by_tiles_x, by_tiles_y, by_n16;
+    int n16cap;            // 16-byte chunks staged per source row, at most
+    int pitch;             // LDS bytes per staged row: 16 (n16cap + 1)
+};
+
+template <int C, int PX, int TH, int KL>
+__global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
+    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W, int dH, int dW,
+    long long src_bytes, TileGeom tg)
+{
+    constexpr int COLS = 64 * PX;
+    constexpr int NT = 64 * kTileWaves;
+    static_assert(TH % kTileWaves == 0 && (PX * C) % 4 == 0, "tile shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
+    uint32_t *const ctab = (uint32_t *)lds_all;      // COLS packed column entries
+    uint8_t *const rows = lds_all + COLS * 4;        // staged rows, tg.pitch bytes apart
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // workgroup -> (image n, row tile ty, column segment tx)
+    const unsigned r1 = fast_div(blockIdx.x, tg.by_tiles_x);
+    const int tx = (int)(blockIdx.x - r1 * (unsigned)tg.tiles_x);
+    const unsigned n = fast_div(r1, tg.by_tiles_y);
+    const int ty = (int)(r1 - n * (unsigned)tg.tiles_y);
+
+    const int wx0 = tx * COLS, wx1 = min(wx0 + COLS, dW) - 1;
+    const int dy0 = ty * TH, dy1 = min(dy0 + TH, dH) - 1;
+    const int sa = axis_tap(wx0, W, dW).a, sb = axis_tap(wx1, W, dW).b;
+    const int ra0 = axis_tap(dy0, H, dH).a, rb1 = axis_tap(dy1, H, dH).b;
+    const int nr = rb1 - ra0 + 1;                    // staged rows, at most the launch's cap
+    const unsigned bytes = (unsigned)(sb - sa + 1) * C;
+    const size_t row_bytes = (size_t)W * C;
+    const uint8_t *const lo = src;
+    const uint8_t *const hi = src + src_bytes;
+    // first needed byte of staged row k: p0 + k row_bytes; its offset in its
+    // 16-byte chunk steps by row_bytes mod 16 from row to row
+    const uint8_t *const p0 =
+        src + ((size_t)n * H + ra0) * row_bytes + (size_t)sa * C;
+    const unsigned mis0 = (unsigned)(uintptr_t)p0 & 15u;
+    const unsigned rstep = (unsigned)(row_bytes & 15u);
+
+    // Stage: chunk i = k n16cap + j is chunk j of staged row k, from the
+    // 16-byte boundary at or below the row's first needed byte.  A row's
+    // chunks end at most 16 n16cap bytes past that boundary, so unless the
+    // tile holds the buffer's first or last rows every chunk lies inside
+    // the source buffer.  Then all loads are issued before any LDS write,
+    // with no branch: a lane past the last chunk repeats it (the same bytes
+    // to the same place).  Tiles at the buffer's ends stage chunk by chunk,
+    // and a chunk that leaves the buffer byte by byte with checks.
+    const int total = nr * tg.n16cap;
+    auto chunk = [&](int i, const uint8_t *&q, int &off) {
+        const int k = (int)fast_div((unsigned)i, tg.by_n16);
+        const int j = i - k * tg.n16cap;
+        const unsigned mis = (mis0 + (unsigned)k * rstep) & 15u;
+        q = p0 + (size_t)k * row_bytes - mis + 16 * j;
+        off = k * tg.pitch + 16 * j;
+    };
+    const unsigned mis_last = (mis0 + (unsigned)(nr - 1) * rstep) & 15u;
+    const bool inside = p0 - mis0 >= lo &&
+                        p0 + (size_t)(nr - 1) * row_bytes - mis_last + 16 * (size_t)tg.n16cap <= hi;
+    if (inside) {
+        u32x4_t v[KL];
+        int loff[KL];
+#pragma unroll
+        for (int t = 0; t < KL; ++t) {
+            const uint8_t *q;
+            chunk(min(tid + t * NT, total - 1), q, loff[t]);
+            v[t] = *(const u32x4_t *)q;
+        }
+#pragma unroll
+        for (int t = 0; t < KL; ++t) *(u32x4_t *)(rows + loff[t]) = v[t];
+    } else {
+#pragma unroll 1
+        for (int i = tid; i < total; i += NT) {
+            const uint8_t *q;
+            int off;
+            chunk(i, q, off);
+            if (q >= lo && q + 16 <= hi) {
+                *(u32x4_t *)(rows + off) = *(const u32x4_t *)q;
+            } else {
+#pragma unroll 1
+                for (int b = 0; b < 16; ++b)
+                    rows[off + b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
+            }
+        }
+    }
+    // the segment's column table; columns past dW - 1 repeat the last one
+    for (int c = tid; c < COLS; c += NT) {
+        const Tap t = axis_tap(min(wx0 + c, dW - 1), W, dW);
+        ctab[c] = ((uint32_t)((t.a - sa) * C) << 13) | ((uint32_t)(t.b != t.a) << 12) |
+                  weight11(t);
+    }
+    __syncthreads();
+
+    int toff[PX];
+    uint32_t twp[PX];
+#pragma unroll
+    for (int p = 0; p < PX; ++p) {
+        const uint32_t e = ctab[lane * PX + p];
+        toff[p] = (int)(e >> 13);
+        twp[p] = weight_pair(e & 4095u, (e >> 12) & 1u);
+    }
+    const int x0 = wx0 + lane * PX;
+    const int valid_px = max(0, min(PX, dW - x0));
+    constexpr int RW = TH / kTileWaves;
+    for (int r = 0; r < RW; ++r) {
+        const int dy = dy0 + wave * RW + r;
+        if (dy > dy1) break;                          // a short last tile (uniform)
+        const Tap t = axis_tap(dy, H, dH);
+        const int ka = t.a - ra0, kb = t.b - ra0;
+        const uint8_t *la = rows + ka * tg.pitch + ((mis0 + (unsigned)ka * rstep) & 15u);
+        const uint8_t *lb = rows + kb * tg.pitch + ((mis0 + (unsigned)kb * rstep) & 15u);
+        const unsigned wy1 = weight11(t);
+        const uint32_t wy0x4 = (2048u - wy1) << 2, wy1x4 = wy1 << 2;
+        uint32_t fx[PX * C];
+#pragma unroll
+        for (int p = 0; p < PX; ++p) {
+            if constexpr (C == 1) {
+                const uint8_t *qa = la + toff[p], *qb = lb + toff[p];
+                fx[p] = blend_u8_pairs((uint32_t)qa[0] | ((uint32_t)qa[1] << 16),
+                                       (uint32_t)qb[0] | ((uint32_t)qb[1] << 16), twp[p], wy0x4,
+                                       wy1x4);
+            } else {
+                uint32_t a_lo, a_hi, b_lo, b_hi;
+                lds_bytes8(la + toff[p], a_lo, a_hi);
+                lds_bytes8(lb + toff[p], b_lo, b_hi);
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const uint32_t sel = 0x0c000c00u | ((uint32_t)(C + c) << 16) | (uint32_t)c;
+                    fx[p * C + c] = blend_u8_pairs(__builtin_amdgcn_perm(a_hi, a_lo, sel),
+                                                   __builtin_amdgcn_perm(b_hi, b_lo, sel), twp[p],
+                                                   wy0x4, wy1x4);
+                }
+            }
+        }
+        uint32_t wds[PX * C / 4];
+#pragma unroll
+        for (int k = 0; k < PX * C / 4; ++k)
+            wds[k] = pack_byte3(fx[4 * k], fx[4 * k + 1], fx[4 * k + 2], fx[4 * k + 3]);
+        uint8_t res[PX * C];
+        __builtin_memcpy(res, wds, sizeof(wds));
+        if (valid_px > 0)
+            store_chunk<uint8_t, PX * C>(dst + (((size_t)n * dH + dy) * dW + x0) * C, res,
+                                         valid_px * C);
+    }
+}
+
+// --------------------------------------------------------------------------
 // Plain copy for bandwidth calibration: 16-byte units, grid-stride, each lane
 // keeping kCopyUnroll loads in flight before it stores them (one load then
 // one store per pass would wait a full memory latency per chunk), with the

@@ -82,7 +82,7 @@ def test_workload_full_size(name, mode):
                   "%s/%s" % (name, mode))
 
 
-PATHS = ["rowseg", "direct"]   # MI_RESIZE_PATH: force one kernel family
+PATHS = ["rowseg", "direct", "tile"]   # MI_RESIZE_PATH: force one kernel family
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -372,6 +372,33 @@ def test_batch_of_tiny_images():
 
 
 # --------------------------------------------------------------------------
+# uint8 row enlargements large enough for the tiled kernel under the default
+# path: 16-row tiles (about 700 or more) and 8-row tiles, batches, ragged
+# last tiles in both directions, one, three and four channels
+# --------------------------------------------------------------------------
+TILE_SHAPES = [
+    (4, 300, 500, 3, 800, 1201),     # 16-row tiles
+    (2, 300, 500, 3, 701, 1100),     # 8-row tiles
+    (1, 500, 900, 4, 1000, 1803),
+    (3, 400, 600, 1, 1003, 1500),
+    (2, 600, 800, 1, 1500, 2000),    # 16-row tiles, one channel
+    (2, 123, 1000, 3, 1300, 1001),   # rows enlarge, columns nearly the same
+    (1, 700, 97, 3, 2100, 291),      # narrow rows, a single column segment
+]
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES)
+def test_tile_enlargements(shape, monkeypatch):
+    monkeypatch.delenv("MI_RESIZE_PATH", raising=False)
+    N, H, W, C, dH, dW = shape
+    say("case tile %s" % (shape,))
+    r = np.random.default_rng(7 + sum(shape))
+    s = random_image(r, (N, H, W, C), "u8")
+    assert_parity(run_gpu(s, dH, dW, "linear"), run_oracle(s, dH, dW, "linear"),
+                  "tile %s" % (shape,))
+
+
+# --------------------------------------------------------------------------
 # misaligned buffers take the scalar paths; results must not change
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("path", ["auto"] + PATHS)
@@ -382,7 +409,8 @@ def test_misaligned_buffers(dtype, mode, path, monkeypatch):
         monkeypatch.setenv("MI_RESIZE_PATH", path)
     r = np.random.default_rng(11)
     es = 1 if dtype == "u8" else 4
-    for (N, H, W, C, dH, dW) in ((1, 64, 64, 4, 32, 32), (2, 40, 64, 3, 20, 32), (1, 33, 47, 1, 70, 20)):
+    for (N, H, W, C, dH, dW) in ((1, 64, 64, 4, 32, 32), (2, 40, 64, 3, 20, 32), (1, 33, 47, 1, 70, 20),
+                                 (1, 400, 700, 3, 800, 1400)):   # the last: a tiled enlargement
         for off in ((1, 3) if dtype == "u8" else (1, 2)):
             say("case misaligned %s %s off=%d %s" % (dtype, mode, off, (N, H, W, C, dH, dW)))
             s_np = random_image(r, (N, H, W, C), dtype)
