@@ -2213,10 +2213,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     // 16-byte boundary at or below the row's first needed byte.  A row's
     // chunks end at most 16 n16cap bytes past that boundary, so unless the
     // tile holds the buffer's first or last rows every chunk lies inside
-    // the source buffer.  Then all loads are issued before any LDS write,
-    // with no branch: a lane past the last chunk repeats it (the same bytes
-    // to the same place).  Tiles at the buffer's ends stage chunk by chunk,
-    // and a chunk that leaves the buffer byte by byte with checks.
+    // the source buffer.  Then the chunks go in rounds of KL per thread,
+    // each round's loads all issued before its LDS writes, with no divergent
+    // branch: a lane past the last chunk repeats it (the same bytes to the
+    // same place), and a round wholly past the tile is skipped (a uniform
+    // test, so a launch sized for its largest tile costs smaller ones
+    // nothing).  Tiles at the buffer's ends stage chunk by chunk, and a
+    // chunk that leaves the buffer byte by byte with checks.
     const int total = nr * tg.n16cap;
     auto chunk = [&](int i, const uint8_t *&q, int &off) {
         const int k = (int)fast_div((unsigned)i, tg.by_n16);
@@ -2229,16 +2232,22 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     const bool inside = p0 - mis0 >= lo &&
                         p0 + (size_t)(nr - 1) * row_bytes - mis_last + 16 * (size_t)tg.n16cap <= hi;
     if (inside) {
-        u32x4_t v[KL];
-        int loff[KL];
+#pragma unroll 1
+        for (int base = 0; base < total; base += KL * NT) {
+            u32x4_t v[KL];
+            int loff[KL];
 #pragma unroll
-        for (int t = 0; t < KL; ++t) {
-            const uint8_t *q;
-            chunk(min(tid + t * NT, total - 1), q, loff[t]);
-            v[t] = *(const u32x4_t *)q;
+            for (int t = 0; t < KL; ++t) {
+                if (base + t * NT < total) {
+                    const uint8_t *q;
+                    chunk(min(base + tid + t * NT, total - 1), q, loff[t]);
+                    v[t] = *(const u32x4_t *)q;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < KL; ++t)
+                if (base + t * NT < total) *(u32x4_t *)(rows + loff[t]) = v[t];
         }
-#pragma unroll
-        for (int t = 0; t < KL; ++t) *(u32x4_t *)(rows + loff[t]) = v[t];
     } else {
 #pragma unroll 1
         for (int i = tid; i < total; i += NT) {
