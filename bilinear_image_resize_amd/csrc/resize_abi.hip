@@ -615,13 +615,18 @@ bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH,
 // 7.25, 1080p -> 1200x1600 RGB 8.52 -> 9.63 / 8.07, 720p -> 900x1200 RGB
 // 6.87 -> 7.52 / 6.32, grey 1080p -> 1620x2880 8.84 -> 7.30 / 7.00; below
 // the floor 480x640 -> 720x960 RGB 4.77 -> 6.08 / 4.98 and 8 x 224^2 ->
-// 256^2 RGB 4.23 -> 6.94 / 5.07.  `forced` (MI_RESIZE_PATH=tile) skips the
-// floor.  Downscales and crop batches stay on the row-segment kernel: a
+// 256^2 RGB 4.23 -> 6.94 / 5.07.  One-channel tiles (512 columns, twice an
+// RGB tile's) pay from fewer of them: grey 1080p -> 1620x2880 6.77 -> 6.43
+// us with 16-row tiles at 612 of them, 600x800 -> 900x1200 5.79 -> 5.09
+// with 8-row tiles at 339 (RGB 1080p -> 1200x1600 lost at 525 16-row tiles,
+// 7.54 -> 9.01).  `forced` (MI_RESIZE_PATH=tile) skips the floor.  Downscales and crop batches stay on the row-segment kernel: a
 // tile there stages about twice the rows it writes before any blend, and
 // the thumbnail batch went 45.1 -> 61.0 us, its random crops 34.8 -> 44.5,
 // 4K -> 1440x2560 RGB 10.2 -> 13.8.
 constexpr long long kTileBlocks16 = 700;
 constexpr long long kTileBlocks8 = 512;
+constexpr long long kTileBlocks16One = 400;   // one channel
+constexpr long long kTileBlocks8One = 200;
 
 template <int C>
 bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
@@ -631,9 +636,11 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
     const long long per_image = (dW + COLS - 1) / COLS;
     const long long b16 = (long long)batch * ((dH + 15) / 16) * per_image;
     const long long b8 = (long long)batch * ((dH + 7) / 8) * per_image;
-    if (b16 >= kTileBlocks16 && launch_tile_u8<C, 16>(src, dst, batch, H, W, dH, dW, st, rc))
+    const long long min16 = C == 1 ? kTileBlocks16One : kTileBlocks16;
+    const long long min8 = C == 1 ? kTileBlocks8One : kTileBlocks8;
+    if (b16 >= min16 && launch_tile_u8<C, 16>(src, dst, batch, H, W, dH, dW, st, rc))
         return true;
-    if (b8 >= kTileBlocks8 || forced)
+    if (b8 >= min8 || forced)
         return launch_tile_u8<C, 8>(src, dst, batch, H, W, dH, dW, st, rc);
     return false;
 }

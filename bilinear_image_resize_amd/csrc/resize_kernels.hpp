@@ -2282,36 +2282,58 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     const int x0 = wx0 + lane * PX;
     const int valid_px = max(0, min(PX, dW - x0));
     constexpr int RW = TH / kTileWaves;
+    // Each staged row's horizontal sums (row_sum_u8 per channel and pixel)
+    // are kept for as long as consecutive output rows use the row: a wave
+    // walks its rows downwards, so the last two rows it summed suffice.
+    constexpr int NH = PX * C;
+    uint32_t hA[NH], hB[NH];
+    int iA = -1, iB = -1;                             // rows held in hA, hB (uniform)
+    auto hrow = [&](int k, uint32_t (&h)[NH]) __attribute__((always_inline)) {
+        const uint8_t *l = rows + k * tg.pitch + ((mis0 + (unsigned)k * rstep) & 15u);
+#pragma unroll
+        for (int p = 0; p < PX; ++p) {
+            if constexpr (C == 1) {
+                const uint8_t *q = l + toff[p];
+                h[p] = row_sum_u8((uint32_t)q[0] | ((uint32_t)q[1] << 16), twp[p]);
+            } else {
+                uint32_t w_lo, w_hi;
+                lds_bytes8(l + toff[p], w_lo, w_hi);
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const uint32_t sel = 0x0c000c00u | ((uint32_t)(C + c) << 16) | (uint32_t)c;
+                    h[p * C + c] = row_sum_u8(__builtin_amdgcn_perm(w_hi, w_lo, sel), twp[p]);
+                }
+            }
+        }
+    };
     for (int r = 0; r < RW; ++r) {
         const int dy = dy0 + wave * RW + r;
         if (dy > dy1) break;                          // a short last tile (uniform)
         const Tap t = axis_tap(dy, H, dH);
         const int ka = t.a - ra0, kb = t.b - ra0;
-        const uint8_t *la = rows + ka * tg.pitch + ((mis0 + (unsigned)ka * rstep) & 15u);
-        const uint8_t *lb = rows + kb * tg.pitch + ((mis0 + (unsigned)kb * rstep) & 15u);
+        if (ka != iA) {
+            if (ka == iB) {
+#pragma unroll
+                for (int k = 0; k < NH; ++k) hA[k] = hB[k];
+            } else {
+                hrow(ka, hA);
+            }
+            iA = ka;
+        }
+        if (kb != iB) {
+            if (kb == iA) {
+#pragma unroll
+                for (int k = 0; k < NH; ++k) hB[k] = hA[k];
+            } else {
+                hrow(kb, hB);
+            }
+            iB = kb;
+        }
         const unsigned wy1 = weight11(t);
         const uint32_t wy0x4 = (2048u - wy1) << 2, wy1x4 = wy1 << 2;
         uint32_t fx[PX * C];
 #pragma unroll
-        for (int p = 0; p < PX; ++p) {
-            if constexpr (C == 1) {
-                const uint8_t *qa = la + toff[p], *qb = lb + toff[p];
-                fx[p] = blend_u8_pairs((uint32_t)qa[0] | ((uint32_t)qa[1] << 16),
-                                       (uint32_t)qb[0] | ((uint32_t)qb[1] << 16), twp[p], wy0x4,
-                                       wy1x4);
-            } else {
-                uint32_t a_lo, a_hi, b_lo, b_hi;
-                lds_bytes8(la + toff[p], a_lo, a_hi);
-                lds_bytes8(lb + toff[p], b_lo, b_hi);
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const uint32_t sel = 0x0c000c00u | ((uint32_t)(C + c) << 16) | (uint32_t)c;
-                    fx[p * C + c] = blend_u8_pairs(__builtin_amdgcn_perm(a_hi, a_lo, sel),
-                                                   __builtin_amdgcn_perm(b_hi, b_lo, sel), twp[p],
-                                                   wy0x4, wy1x4);
-                }
-            }
-        }
+        for (int k = 0; k < NH; ++k) fx[k] = col_sum_u8(hA[k], hB[k], wy0x4, wy1x4);
         uint32_t wds[PX * C / 4];
 #pragma unroll
         for (int k = 0; k < PX * C / 4; ++k)
