@@ -565,9 +565,9 @@ int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, 
 // false otherwise (the caller then picks another kernel).
 constexpr long long kTileLdsBudget = 64 * 1024;
 
-template <int C, int TH>
+template <int C, int TH, bool NEAREST>
 bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                    hipStream_t st, int &rc)
+                    hipStream_t st, int &rc, int nn_map)
 {
     constexpr int PX = C == 1 ? 8 : 4;
     constexpr int COLS = 64 * PX;
@@ -594,14 +594,14 @@ bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH,
     const long long src_bytes = (long long)batch * H * W * C;
     auto go = [&](auto kernel) {
         rc = launch(kernel, dim3((unsigned)blocks), dim3(64 * kTileWaves), (unsigned)lds, st,
-                    (const uint8_t *)src, (uint8_t *)dst, H, W, dH, dW, src_bytes, tg);
+                    (const uint8_t *)src, (uint8_t *)dst, H, W, dH, dW, src_bytes, tg, nn_map);
         return true;
     };
     // chunks per thread and staging round (more rounds where a tile needs them)
-    if (chunks <= 1) return go(tile_u8<C, PX, TH, 1>);
-    if (chunks <= 2) return go(tile_u8<C, PX, TH, 2>);
-    if (chunks <= 4) return go(tile_u8<C, PX, TH, 4>);
-    return go(tile_u8<C, PX, TH, 8>);
+    if (chunks <= 1) return go(tile_u8<C, PX, TH, 1, NEAREST>);
+    if (chunks <= 2) return go(tile_u8<C, PX, TH, 2, NEAREST>);
+    if (chunks <= 4) return go(tile_u8<C, PX, TH, 4, NEAREST>);
+    return go(tile_u8<C, PX, TH, 8, NEAREST>);
 }
 
 // The tile height by the launch's size.  A tile runs one memory round trip
@@ -628,9 +628,9 @@ constexpr long long kTileBlocks8 = 512;
 constexpr long long kTileBlocks16One = 400;   // one channel
 constexpr long long kTileBlocks8One = 200;
 
-template <int C>
+template <int C, bool NEAREST = false>
 bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                 hipStream_t st, int &rc, bool forced)
+                 hipStream_t st, int &rc, bool forced, int nn_map = kNearestHalfPixel)
 {
     constexpr int COLS = 64 * (C == 1 ? 8 : 4);
     const long long per_image = (dW + COLS - 1) / COLS;
@@ -638,10 +638,11 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
     const long long b8 = (long long)batch * ((dH + 7) / 8) * per_image;
     const long long min16 = C == 1 ? kTileBlocks16One : kTileBlocks16;
     const long long min8 = C == 1 ? kTileBlocks8One : kTileBlocks8;
-    if (b16 >= min16 && launch_tile_u8<C, 16>(src, dst, batch, H, W, dH, dW, st, rc))
+    if (b16 >= min16 &&
+        launch_tile_u8<C, 16, NEAREST>(src, dst, batch, H, W, dH, dW, st, rc, nn_map))
         return true;
     if (b8 >= min8 || forced)
-        return launch_tile_u8<C, 8>(src, dst, batch, H, W, dH, dW, st, rc);
+        return launch_tile_u8<C, 8, NEAREST>(src, dst, batch, H, W, dH, dW, st, rc, nn_map);
     return false;
 }
 
@@ -683,9 +684,16 @@ int nearest_dispatch(const void *src, void *dst, int batch, int H, int W, int dH
     }
     int rc;
     const bool small = small_launch(batch, H, W, dH, dW);
+    if constexpr (sizeof(T) == 1) {
+        // row enlargements: the tiled kernel
+        if (path == Path::Tile || (path == Path::Auto && !small && dH >= H))
+            if (try_tile_u8<C, true>(src, dst, batch, H, W, dH, dW, st, rc, path == Path::Tile,
+                                     map))
+                return rc;
+    }
     // float RGB / RGBA enlargements: the direct kernel, as for linear
     // (1080p RGBA 2x 26.4 vs 41.8 us, RGB 2x 23.0 vs 87.1 us)
-    if (path == Path::RowSeg ||
+    if (path == Path::RowSeg || path == Path::Tile ||
         (path == Path::Auto && !small && !prefer_direct<T, C>(W, dW)))
         if (try_rowseg<T, C, true>(src, dst, batch, H, W, dH, dW, st, rc, Affine{}, nullptr, map))
             return rc;

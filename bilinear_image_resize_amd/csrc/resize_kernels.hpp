@@ -2172,10 +2172,10 @@ struct TileGeom {
     int pitch;             // LDS bytes per staged row: 16 (n16cap + 1)
 };
 
-template <int C, int PX, int TH, int KL>
+template <int C, int PX, int TH, int KL, bool NEAREST>
 __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W, int dH, int dW,
-    long long src_bytes, TileGeom tg)
+    long long src_bytes, TileGeom tg, int nn_map)
 {
     constexpr int COLS = 64 * PX;
     constexpr int NT = 64 * kTileWaves;
@@ -2195,8 +2195,20 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
 
     const int wx0 = tx * COLS, wx1 = min(wx0 + COLS, dW) - 1;
     const int dy0 = ty * TH, dy1 = min(dy0 + TH, dH) - 1;
-    const int sa = axis_tap(wx0, W, dW).a, sb = axis_tap(wx1, W, dW).b;
-    const int ra0 = axis_tap(dy0, H, dH).a, rb1 = axis_tap(dy1, H, dH).b;
+    // source columns [sa, sb] and rows [ra0, rb1] the tile touches (both
+    // maps are non-decreasing, so the end points bound them)
+    int sa, sb, ra0, rb1;
+    if constexpr (NEAREST) {
+        sa = nearest_index(wx0, W, dW, nn_map);
+        sb = nearest_index(wx1, W, dW, nn_map);
+        ra0 = nearest_index(dy0, H, dH, nn_map);
+        rb1 = nearest_index(dy1, H, dH, nn_map);
+    } else {
+        sa = axis_tap(wx0, W, dW).a;
+        sb = axis_tap(wx1, W, dW).b;
+        ra0 = axis_tap(dy0, H, dH).a;
+        rb1 = axis_tap(dy1, H, dH).b;
+    }
     const int nr = rb1 - ra0 + 1;                    // staged rows, at most the launch's cap
     const unsigned bytes = (unsigned)(sb - sa + 1) * C;
     const size_t row_bytes = (size_t)W * C;
@@ -2263,11 +2275,16 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
             }
         }
     }
-    // the segment's column table; columns past dW - 1 repeat the last one
+    // the segment's column table (nearest: the byte offset alone); columns
+    // past dW - 1 repeat the last one
     for (int c = tid; c < COLS; c += NT) {
-        const Tap t = axis_tap(min(wx0 + c, dW - 1), W, dW);
-        ctab[c] = ((uint32_t)((t.a - sa) * C) << 13) | ((uint32_t)(t.b != t.a) << 12) |
-                  weight11(t);
+        if constexpr (NEAREST) {
+            ctab[c] = (uint32_t)((nearest_index(min(wx0 + c, dW - 1), W, dW, nn_map) - sa) * C);
+        } else {
+            const Tap t = axis_tap(min(wx0 + c, dW - 1), W, dW);
+            ctab[c] = ((uint32_t)((t.a - sa) * C) << 13) | ((uint32_t)(t.b != t.a) << 12) |
+                      weight11(t);
+        }
     }
     __syncthreads();
 
@@ -2276,12 +2293,41 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
 #pragma unroll
     for (int p = 0; p < PX; ++p) {
         const uint32_t e = ctab[lane * PX + p];
-        toff[p] = (int)(e >> 13);
+        toff[p] = NEAREST ? (int)e : (int)(e >> 13);
         twp[p] = weight_pair(e & 4095u, (e >> 12) & 1u);
     }
     const int x0 = wx0 + lane * PX;
     const int valid_px = max(0, min(PX, dW - x0));
     constexpr int RW = TH / kTileWaves;
+    if constexpr (NEAREST) {
+        // one source row per output row; an output row that maps to the
+        // same source row as the one before repeats its bytes
+        uint8_t res[PX * C];
+        int iK = -1;                                  // staged row held in res (uniform)
+        for (int r = 0; r < RW; ++r) {
+            const int dy = dy0 + wave * RW + r;
+            if (dy > dy1) break;                      // a short last tile (uniform)
+            const int k = nearest_index(dy, H, dH, nn_map) - ra0;
+            if (k != iK) {
+                const uint8_t *l = rows + k * tg.pitch + ((mis0 + (unsigned)k * rstep) & 15u);
+#pragma unroll
+                for (int p = 0; p < PX; ++p) {
+                    if constexpr (C == 1) {
+                        res[p] = l[toff[p]];
+                    } else {
+                        const uint32_t w = lds_bytes4(l + toff[p]);
+#pragma unroll
+                        for (int c = 0; c < C; ++c) res[p * C + c] = (uint8_t)(w >> (8 * c));
+                    }
+                }
+                iK = k;
+            }
+            if (valid_px > 0)
+                store_chunk<uint8_t, PX * C>(dst + (((size_t)n * dH + dy) * dW + x0) * C, res,
+                                             valid_px * C);
+        }
+        return;
+    }
     // Each staged row's horizontal sums (row_sum_u8 per channel and pixel)
     // are kept for as long as consecutive output rows use the row: a wave
     // walks its rows downwards, so the last two rows it summed suffice.
