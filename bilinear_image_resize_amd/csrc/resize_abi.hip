@@ -565,7 +565,7 @@ int launch_nearest(const void *src, void *dst, int batch, int H, int W, int dH, 
 // false otherwise (the caller then picks another kernel).
 constexpr long long kTileLdsBudget = 64 * 1024;
 
-template <int C, int TH, bool NEAREST>
+template <int C, int TH, bool NEAREST, int OUT>
 bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                     hipStream_t st, int &rc, int nn_map)
 {
@@ -598,10 +598,10 @@ bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH,
         return true;
     };
     // chunks per thread and staging round (more rounds where a tile needs them)
-    if (chunks <= 1) return go(tile_u8<C, PX, TH, 1, NEAREST>);
-    if (chunks <= 2) return go(tile_u8<C, PX, TH, 2, NEAREST>);
-    if (chunks <= 4) return go(tile_u8<C, PX, TH, 4, NEAREST>);
-    return go(tile_u8<C, PX, TH, 8, NEAREST>);
+    if (chunks <= 1) return go(tile_u8<C, PX, TH, 1, NEAREST, OUT>);
+    if (chunks <= 2) return go(tile_u8<C, PX, TH, 2, NEAREST, OUT>);
+    if (chunks <= 4) return go(tile_u8<C, PX, TH, 4, NEAREST, OUT>);
+    return go(tile_u8<C, PX, TH, 8, NEAREST, OUT>);
 }
 
 // The tile height by the launch's size.  A tile runs one memory round trip
@@ -628,7 +628,7 @@ constexpr long long kTileBlocks8 = 512;
 constexpr long long kTileBlocks16One = 400;   // one channel
 constexpr long long kTileBlocks8One = 200;
 
-template <int C, bool NEAREST = false>
+template <int C, bool NEAREST = false, int OUT = kOutSame>
 bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                  hipStream_t st, int &rc, bool forced, int nn_map = kNearestHalfPixel)
 {
@@ -639,10 +639,10 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
     const long long min16 = C == 1 ? kTileBlocks16One : kTileBlocks16;
     const long long min8 = C == 1 ? kTileBlocks8One : kTileBlocks8;
     if (b16 >= min16 &&
-        launch_tile_u8<C, 16, NEAREST>(src, dst, batch, H, W, dH, dW, st, rc, nn_map))
+        launch_tile_u8<C, 16, NEAREST, OUT>(src, dst, batch, H, W, dH, dW, st, rc, nn_map))
         return true;
     if (b8 >= min8 || forced)
-        return launch_tile_u8<C, 8, NEAREST>(src, dst, batch, H, W, dH, dW, st, rc, nn_map);
+        return launch_tile_u8<C, 8, NEAREST, OUT>(src, dst, batch, H, W, dH, dW, st, rc, nn_map);
     return false;
 }
 
@@ -774,7 +774,14 @@ int grey_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, i
     }
     const bool small = small_launch(batch, H, W, dH, dW);
     int rc;
-    if (path == Path::RowSeg || (path == Path::Auto && !small))
+    if constexpr (sizeof(T) == 1) {
+        // row enlargements: the tiled kernel
+        if (path == Path::Tile || (path == Path::Auto && !small && dH >= H))
+            if (try_tile_u8<C, false, kOutGrey>(src, dst, batch, H, W, dH, dW, st, rc,
+                                                path == Path::Tile))
+                return rc;
+    }
+    if (path == Path::RowSeg || path == Path::Tile || (path == Path::Auto && !small))
         if (try_rowseg<T, C, false, kOutGrey>(src, dst, batch, H, W, dH, dW, st, rc)) return rc;
     const Grid g = band_grid(rows, dW, dH);
     return launch(linear_generic<T, C, false, kOutGrey>, dim3(g.blocks), dim3(kBlock), 0, st,

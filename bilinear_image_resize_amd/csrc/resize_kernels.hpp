@@ -2172,7 +2172,7 @@ struct TileGeom {
     int pitch;             // LDS bytes per staged row: 16 (n16cap + 1)
 };
 
-template <int C, int PX, int TH, int KL, bool NEAREST>
+template <int C, int PX, int TH, int KL, bool NEAREST, int OUT>
 __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W, int dH, int dW,
     long long src_bytes, TileGeom tg, int nn_map)
@@ -2180,6 +2180,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     constexpr int COLS = 64 * PX;
     constexpr int NT = 64 * kTileWaves;
     static_assert(TH % kTileWaves == 0 && (PX * C) % 4 == 0, "tile shape");
+    static_assert(OUT == kOutSame || (OUT == kOutGrey && !NEAREST && C >= 3), "tile output");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
     uint32_t *const ctab = (uint32_t *)lds_all;      // COLS packed column entries
     uint8_t *const rows = lds_all + COLS * 4;        // staged rows, tg.pitch bytes apart
@@ -2328,10 +2329,11 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
         }
         return;
     }
-    // Each staged row's horizontal sums (row_sum_u8 per channel and pixel)
-    // are kept for as long as consecutive output rows use the row: a wave
-    // walks its rows downwards, so the last two rows it summed suffice.
-    constexpr int NH = PX * C;
+    // Each staged row's horizontal sums (row_sum_u8 per channel and pixel,
+    // or per pixel of grey values for grey output) are kept for as long as
+    // consecutive output rows use the row: a wave walks its rows downwards,
+    // so the last two rows it summed suffice.
+    constexpr int NH = OUT == kOutGrey ? PX : PX * C;
     uint32_t hA[NH], hB[NH];
     int iA = -1, iB = -1;                             // rows held in hA, hB (uniform)
     auto hrow = [&](int k, uint32_t (&h)[NH]) __attribute__((always_inline)) {
@@ -2341,6 +2343,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
             if constexpr (C == 1) {
                 const uint8_t *q = l + toff[p];
                 h[p] = row_sum_u8((uint32_t)q[0] | ((uint32_t)q[1] << 16), twp[p]);
+            } else if constexpr (OUT == kOutGrey) {
+                // both taps to grey first (tap b at byte C), then the sum
+                uint32_t w_lo, w_hi;
+                lds_bytes8(l + toff[p], w_lo, w_hi);
+                auto gr = [](uint32_t w) {
+                    return grey_u8(w & 255u, (w >> 8) & 255u, (w >> 16) & 255u);
+                };
+                const uint32_t w2 = C == 4 ? w_hi : __builtin_amdgcn_alignbyte(w_hi, w_lo, C);
+                h[p] = row_sum_u8(gr(w_lo) | (gr(w2) << 16), twp[p]);
             } else {
                 uint32_t w_lo, w_hi;
                 lds_bytes8(l + toff[p], w_lo, w_hi);
@@ -2377,9 +2388,17 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
         }
         const unsigned wy1 = weight11(t);
         const uint32_t wy0x4 = (2048u - wy1) << 2, wy1x4 = wy1 << 2;
-        uint32_t fx[PX * C];
+        uint32_t fx[NH];
 #pragma unroll
         for (int k = 0; k < NH; ++k) fx[k] = col_sum_u8(hA[k], hB[k], wy0x4, wy1x4);
+        if constexpr (OUT == kOutGrey) {
+            uint8_t resg[PX];
+#pragma unroll
+            for (int p = 0; p < PX; ++p) resg[p] = (uint8_t)(fx[p] >> 24);
+            if (valid_px > 0)
+                store_chunk<uint8_t, PX>(dst + ((size_t)n * dH + dy) * dW + x0, resg, valid_px);
+            continue;
+        }
         uint32_t wds[PX * C / 4];
 #pragma unroll
         for (int k = 0; k < PX * C / 4; ++k)

@@ -398,6 +398,20 @@ def test_tile_enlargements(shape, monkeypatch):
                   "tile %s" % (shape,))
 
 
+@pytest.mark.parametrize("shape", [(1, 540, 960, 3, 1080, 1700),     # 8-row tiles
+                                   (2, 600, 800, 4, 1200, 1601)])   # 16-row tiles
+def test_tile_grey_enlargements(shape, monkeypatch):
+    monkeypatch.delenv("MI_RESIZE_PATH", raising=False)
+    N, H, W, C, dH, dW = shape
+    say("case tile grey %s" % (shape,))
+    s = random_image(np.random.default_rng(5 + sum(shape)), (N, H, W, C), "u8")
+    src = torch.from_numpy(s).cuda()
+    dst = torch.empty((N, dH, dW, 1), dtype=src.dtype, device="cuda")
+    R.resize_linear_grey(src, dst)
+    torch.cuda.synchronize()
+    assert_parity(dst.cpu().numpy(), oracle.resize_linear_grey(s, dH, dW), "tile grey %s" % (shape,))
+
+
 # --------------------------------------------------------------------------
 # misaligned buffers take the scalar paths; results must not change
 # --------------------------------------------------------------------------
