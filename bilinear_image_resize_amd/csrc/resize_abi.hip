@@ -646,6 +646,63 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
     return false;
 }
 
+// One-channel float32 linear row enlargements on tile_f32: the geometry,
+// budget and tile-height rule of the uint8 tiles, 8 pixels per lane (tiles
+// of 512 columns).  Grey 1080p -> 1620x2880: 13.55 -> 9.51 us against the
+// row-segment kernel.
+template <int C, int TH>
+bool launch_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                     hipStream_t st, int &rc)
+{
+    constexpr int PX = C == 1 ? 8 : (C == 3 ? 4 : 2);
+    constexpr int COLS = 64 * PX;
+    constexpr int PB = 4 * C;
+    long long span = (long long)(COLS - 1) * W / dW + 3;
+    if (span > W) span = W;
+    const long long n16cap = (15 + span * PB + 15) >> 4;
+    const long long pitch = 16 * (n16cap + 1);
+    const long long rows_cap = (long long)(TH - 1) * H / dH + 3;
+    const long long lds = (long long)COLS * 8 + rows_cap * pitch + 16;
+    if (lds > kTileLdsBudget) return false;
+    const long long chunks = (rows_cap * n16cap + 255) / 256;
+    const int tiles_x = (dW + COLS - 1) / COLS, tiles_y = (dH + TH - 1) / TH;
+    const long long blocks = (long long)batch * tiles_y * tiles_x;
+    if (blocks >= (1LL << 31)) return false;
+    TileGeom tg;
+    tg.tiles_x = tiles_x;
+    tg.tiles_y = tiles_y;
+    tg.by_tiles_x = fast_div_for(tiles_x);
+    tg.by_tiles_y = fast_div_for(tiles_y);
+    tg.by_n16 = fast_div_for(n16cap);
+    tg.n16cap = (int)n16cap;
+    tg.pitch = (int)pitch;
+    const long long src_bytes = (long long)batch * H * W * PB;
+    auto go = [&](auto kernel) {
+        rc = launch(kernel, dim3((unsigned)blocks), dim3(64 * kTileWaves), (unsigned)lds, st,
+                    (const float *)src, (float *)dst, H, W, dH, dW, src_bytes, tg);
+        return true;
+    };
+    if (chunks <= 1) return go(tile_f32<C, PX, TH, 1>);
+    if (chunks <= 2) return go(tile_f32<C, PX, TH, 2>);
+    if (chunks <= 4) return go(tile_f32<C, PX, TH, 4>);
+    return go(tile_f32<C, PX, TH, 8>);
+}
+
+template <int C>
+bool try_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
+                  hipStream_t st, int &rc, bool forced)
+{
+    constexpr int COLS = 64 * (C == 1 ? 8 : (C == 3 ? 4 : 2));
+    const long long per_image = (dW + COLS - 1) / COLS;
+    const long long b16 = (long long)batch * ((dH + 15) / 16) * per_image;
+    const long long b8 = (long long)batch * ((dH + 7) / 8) * per_image;
+    if (b16 >= kTileBlocks16 && launch_tile_f32<C, 16>(src, dst, batch, H, W, dH, dW, st, rc))
+        return true;
+    if (b8 >= kTileBlocks8 || forced)
+        return launch_tile_f32<C, 8>(src, dst, batch, H, W, dH, dW, st, rc);
+    return false;
+}
+
 template <typename T, int C>
 int linear_dispatch(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                     hipStream_t st)
@@ -659,11 +716,15 @@ int linear_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
     }
     int rc;
     const bool small = small_launch(batch, H, W, dH, dW);
-    if constexpr (sizeof(T) == 1) {
-        // row enlargements: the tiled kernel
-        if (path == Path::Tile || (path == Path::Auto && !small && dH >= H))
+    // row enlargements: the tiled kernels
+    if (path == Path::Tile || (path == Path::Auto && !small && dH >= H)) {
+        if constexpr (sizeof(T) == 1) {
             if (try_tile_u8<C>(src, dst, batch, H, W, dH, dW, st, rc, path == Path::Tile))
                 return rc;
+        } else if constexpr (C == 1) {
+            if (try_tile_f32<C>(src, dst, batch, H, W, dH, dW, st, rc, path == Path::Tile))
+                return rc;
+        }
     }
     if (path == Path::RowSeg || path == Path::Tile ||
         (path == Path::Auto && !small && !prefer_direct<T, C>(W, dW)))

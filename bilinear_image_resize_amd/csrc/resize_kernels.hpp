@@ -2172,6 +2172,74 @@ struct TileGeom {
     int pitch;             // LDS bytes per staged row: 16 (n16cap + 1)
 };
 
+// Stages a tile's nr source rows into LDS, row k at rows + k tg.pitch: the
+// row's first needed byte is p0 + k row_bytes, at offset (mis0 + k rstep)
+// mod 16 in its 16-byte chunk, and the row's chunks from that boundary on
+// (tg.n16cap of them) are copied whole.
+template <int KL>
+__device__ __forceinline__ void tile_stage(uint8_t *rows, const uint8_t *p0, unsigned mis0,
+                                           unsigned rstep, size_t row_bytes, int nr,
+                                           const TileGeom &tg, const uint8_t *lo,
+                                           const uint8_t *hi)
+{
+    // Stage: chunk i = k n16cap + j is chunk j of staged row k, from the
+    // 16-byte boundary at or below the row's first needed byte.  A row's
+    // chunks end at most 16 n16cap bytes past that boundary, so unless the
+    // tile holds the buffer's first or last rows every chunk lies inside
+    // the source buffer.  Then the chunks go in rounds of KL per thread,
+    // each round's loads all issued before its LDS writes, with no divergent
+    // branch: a lane past the last chunk repeats it (the same bytes to the
+    // same place), and a round wholly past the tile is skipped (a uniform
+    // test, so a launch sized for its largest tile costs smaller ones
+    // nothing).  Tiles at the buffer's ends stage chunk by chunk, and a
+    // chunk that leaves the buffer byte by byte with checks.
+    constexpr int NT = 64 * kTileWaves;
+    const int tid = (int)threadIdx.x;
+    const int total = nr * tg.n16cap;
+    auto chunk = [&](int i, const uint8_t *&q, int &off) {
+        const int k = (int)fast_div((unsigned)i, tg.by_n16);
+        const int j = i - k * tg.n16cap;
+        const unsigned mis = (mis0 + (unsigned)k * rstep) & 15u;
+        q = p0 + (size_t)k * row_bytes - mis + 16 * j;
+        off = k * tg.pitch + 16 * j;
+    };
+    const unsigned mis_last = (mis0 + (unsigned)(nr - 1) * rstep) & 15u;
+    const bool inside = p0 - mis0 >= lo &&
+                        p0 + (size_t)(nr - 1) * row_bytes - mis_last + 16 * (size_t)tg.n16cap <= hi;
+    if (inside) {
+#pragma unroll 1
+        for (int base = 0; base < total; base += KL * NT) {
+            u32x4_t v[KL];
+            int loff[KL];
+#pragma unroll
+            for (int t = 0; t < KL; ++t) {
+                if (base + t * NT < total) {
+                    const uint8_t *q;
+                    chunk(min(base + tid + t * NT, total - 1), q, loff[t]);
+                    v[t] = *(const u32x4_t *)q;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < KL; ++t)
+                if (base + t * NT < total) *(u32x4_t *)(rows + loff[t]) = v[t];
+        }
+    } else {
+#pragma unroll 1
+        for (int i = tid; i < total; i += NT) {
+            const uint8_t *q;
+            int off;
+            chunk(i, q, off);
+            if (q >= lo && q + 16 <= hi) {
+                *(u32x4_t *)(rows + off) = *(const u32x4_t *)q;
+            } else {
+#pragma unroll 1
+                for (int b = 0; b < 16; ++b)
+                    rows[off + b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
+            }
+        }
+    }
+}
+
 template <int C, int PX, int TH, int KL, bool NEAREST, int OUT>
 __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int H, int W, int dH, int dW,
@@ -2222,60 +2290,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
     const unsigned mis0 = (unsigned)(uintptr_t)p0 & 15u;
     const unsigned rstep = (unsigned)(row_bytes & 15u);
 
-    // Stage: chunk i = k n16cap + j is chunk j of staged row k, from the
-    // 16-byte boundary at or below the row's first needed byte.  A row's
-    // chunks end at most 16 n16cap bytes past that boundary, so unless the
-    // tile holds the buffer's first or last rows every chunk lies inside
-    // the source buffer.  Then the chunks go in rounds of KL per thread,
-    // each round's loads all issued before its LDS writes, with no divergent
-    // branch: a lane past the last chunk repeats it (the same bytes to the
-    // same place), and a round wholly past the tile is skipped (a uniform
-    // test, so a launch sized for its largest tile costs smaller ones
-    // nothing).  Tiles at the buffer's ends stage chunk by chunk, and a
-    // chunk that leaves the buffer byte by byte with checks.
-    const int total = nr * tg.n16cap;
-    auto chunk = [&](int i, const uint8_t *&q, int &off) {
-        const int k = (int)fast_div((unsigned)i, tg.by_n16);
-        const int j = i - k * tg.n16cap;
-        const unsigned mis = (mis0 + (unsigned)k * rstep) & 15u;
-        q = p0 + (size_t)k * row_bytes - mis + 16 * j;
-        off = k * tg.pitch + 16 * j;
-    };
-    const unsigned mis_last = (mis0 + (unsigned)(nr - 1) * rstep) & 15u;
-    const bool inside = p0 - mis0 >= lo &&
-                        p0 + (size_t)(nr - 1) * row_bytes - mis_last + 16 * (size_t)tg.n16cap <= hi;
-    if (inside) {
-#pragma unroll 1
-        for (int base = 0; base < total; base += KL * NT) {
-            u32x4_t v[KL];
-            int loff[KL];
-#pragma unroll
-            for (int t = 0; t < KL; ++t) {
-                if (base + t * NT < total) {
-                    const uint8_t *q;
-                    chunk(min(base + tid + t * NT, total - 1), q, loff[t]);
-                    v[t] = *(const u32x4_t *)q;
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < KL; ++t)
-                if (base + t * NT < total) *(u32x4_t *)(rows + loff[t]) = v[t];
-        }
-    } else {
-#pragma unroll 1
-        for (int i = tid; i < total; i += NT) {
-            const uint8_t *q;
-            int off;
-            chunk(i, q, off);
-            if (q >= lo && q + 16 <= hi) {
-                *(u32x4_t *)(rows + off) = *(const u32x4_t *)q;
-            } else {
-#pragma unroll 1
-                for (int b = 0; b < 16; ++b)
-                    rows[off + b] = (q + b >= lo && q + b < hi) ? q[b] : (uint8_t)0;
-            }
-        }
-    }
+    tile_stage<KL>(rows, p0, mis0, rstep, row_bytes, nr, tg, lo, hi);
     // the segment's column table (nearest: the byte offset alone); columns
     // past dW - 1 repeat the last one
     for (int c = tid; c < COLS; c += NT) {
@@ -2408,6 +2423,116 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
         if (valid_px > 0)
             store_chunk<uint8_t, PX * C>(dst + (((size_t)n * dH + dy) * dW + x0) * C, res,
                                          valid_px * C);
+    }
+}
+
+// Row enlargements of float32 images by 2-D tiles (linear, clamp): the tile
+// geometry and staging of tile_u8, and blend_f32's arithmetic - the
+// horizontal lerp of each source row (kept across output rows, as in
+// tile_u8), then the vertical lerp - so the results equal the other
+// kernels' bit for bit.  The column table holds two words per column: the
+// byte offset of tap a from column sa << 1 | whether tap b is the next
+// column, and the weight's bits.  Source rows are 4-byte aligned, and so
+// is every staged pixel.  Launched for one channel: float RGB and RGBA
+// enlargements measured faster on the direct kernel, which gathers their
+// 12- and 16-byte pixels from cache and stages its stores (1080p ->
+// 1620x2880 RGBA 20.7 against 21.9 us here with staged stores, 31.6
+// without; 720p -> 1080p RGB 9.1 against 10.1 / 17.8).
+template <int C, int PX, int TH, int KL>
+__global__ __launch_bounds__(64 * kTileWaves) void tile_f32(
+    const float *__restrict__ src, float *__restrict__ dst, int H, int W, int dH, int dW,
+    long long src_bytes, TileGeom tg)
+{
+    constexpr int COLS = 64 * PX;
+    constexpr int NT = 64 * kTileWaves;
+    constexpr int PB = 4 * C;                        // bytes per pixel
+    static_assert(TH % kTileWaves == 0, "tile shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
+    uint32_t *const ctab = (uint32_t *)lds_all;      // 2 COLS words
+    uint8_t *const rows = lds_all + COLS * 8;        // staged rows, tg.pitch bytes apart
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const unsigned r1 = fast_div(blockIdx.x, tg.by_tiles_x);
+    const int tx = (int)(blockIdx.x - r1 * (unsigned)tg.tiles_x);
+    const unsigned n = fast_div(r1, tg.by_tiles_y);
+    const int ty = (int)(r1 - n * (unsigned)tg.tiles_y);
+    const int wx0 = tx * COLS, wx1 = min(wx0 + COLS, dW) - 1;
+    const int dy0 = ty * TH, dy1 = min(dy0 + TH, dH) - 1;
+    const int sa = axis_tap(wx0, W, dW).a;
+    const int ra0 = axis_tap(dy0, H, dH).a, rb1 = axis_tap(dy1, H, dH).b;
+    const int nr = rb1 - ra0 + 1;
+    const size_t row_bytes = (size_t)W * PB;
+    const uint8_t *const lo = (const uint8_t *)src;
+    const uint8_t *const p0 = lo + ((size_t)n * H + ra0) * row_bytes + (size_t)sa * PB;
+    const unsigned mis0 = (unsigned)(uintptr_t)p0 & 15u;
+    const unsigned rstep = (unsigned)(row_bytes & 15u);
+    tile_stage<KL>(rows, p0, mis0, rstep, row_bytes, nr, tg, lo, lo + src_bytes);
+    for (int c = tid; c < COLS; c += NT) {
+        const Tap t = axis_tap(min(wx0 + c, dW - 1), W, dW);
+        ctab[2 * c] = ((uint32_t)((t.a - sa) * PB) << 1) | (uint32_t)(t.b != t.a);
+        ctab[2 * c + 1] = __builtin_bit_cast(uint32_t, weightf(t));
+    }
+    __syncthreads();
+
+    int toff[PX];
+    bool tnext[PX];
+    float wx[PX];
+#pragma unroll
+    for (int p = 0; p < PX; ++p) {
+        const uint32_t e = ctab[2 * (lane * PX + p)];
+        toff[p] = (int)(e >> 1);
+        tnext[p] = e & 1u;
+        wx[p] = __builtin_bit_cast(float, ctab[2 * (lane * PX + p) + 1]);
+    }
+    const int x0 = wx0 + lane * PX;
+    const int valid_px = max(0, min(PX, dW - x0));
+    constexpr int RW = TH / kTileWaves;
+    constexpr int NH = PX * C;
+    float hA[NH], hB[NH];
+    int iA = -1, iB = -1;                             // rows held in hA, hB (uniform)
+    auto hrow = [&](int k, float (&h)[NH]) __attribute__((always_inline)) {
+        const uint8_t *l = rows + k * tg.pitch + ((mis0 + (unsigned)k * rstep) & 15u);
+#pragma unroll
+        for (int p = 0; p < PX; ++p) {
+            const float *q = (const float *)__builtin_assume_aligned(l + toff[p], 4);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const float a = q[c], b = tnext[p] ? q[C + c] : a;
+                h[p * C + c] = fmaf(wx[p], b - a, a);
+            }
+        }
+    };
+    for (int r = 0; r < RW; ++r) {
+        const int dy = dy0 + wave * RW + r;
+        if (dy > dy1) break;                          // a short last tile (uniform)
+        const Tap t = axis_tap(dy, H, dH);
+        const int ka = t.a - ra0, kb = t.b - ra0;
+        if (ka != iA) {
+            if (ka == iB) {
+#pragma unroll
+                for (int k = 0; k < NH; ++k) hA[k] = hB[k];
+            } else {
+                hrow(ka, hA);
+            }
+            iA = ka;
+        }
+        if (kb != iB) {
+            if (kb == iA) {
+#pragma unroll
+                for (int k = 0; k < NH; ++k) hB[k] = hA[k];
+            } else {
+                hrow(kb, hB);
+            }
+            iB = kb;
+        }
+        const float wy = weightf(t);
+        float res[NH];
+#pragma unroll
+        for (int k = 0; k < NH; ++k) res[k] = fmaf(wy, hB[k] - hA[k], hA[k]);
+        if (valid_px > 0)
+            store_chunk<float, NH>(dst + (((size_t)n * dH + dy) * dW + x0) * C, res, valid_px * C);
     }
 }
 

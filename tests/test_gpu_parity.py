@@ -398,6 +398,17 @@ def test_tile_enlargements(shape, monkeypatch):
                   "tile %s" % (shape,))
 
 
+# one-channel float32 row enlargements: the float tiles (8 and 16 rows)
+@pytest.mark.parametrize("shape", [(2, 300, 500, 1, 800, 1300), (4, 300, 600, 1, 900, 1601)])
+def test_tile_enlargements_f32(shape, monkeypatch):
+    monkeypatch.delenv("MI_RESIZE_PATH", raising=False)
+    N, H, W, C, dH, dW = shape
+    say("case tile f32 %s" % (shape,))
+    s = random_image(np.random.default_rng(3 + sum(shape)), (N, H, W, C), "f32")
+    assert_parity(run_gpu(s, dH, dW, "linear"), run_oracle(s, dH, dW, "linear"),
+                  "tile f32 %s" % (shape,))
+
+
 @pytest.mark.parametrize("shape", [(1, 540, 960, 3, 1080, 1700),     # 8-row tiles
                                    (2, 600, 800, 4, 1200, 1601)])   # 16-row tiles
 def test_tile_grey_enlargements(shape, monkeypatch):
