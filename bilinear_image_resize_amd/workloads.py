@@ -14,11 +14,14 @@ small  1 x 48 x 64 x 1, uint8           72 x 96       linear   1001
 up2x   1 x 1080 x 1920 x 1, uint8       2160 x 3840   both     1003
 thumb  256 x 480 x 640 x 3, uint8       224 x 224     linear   1004
 rgbaf  1 x 4320 x 7680 x 4, float32     5927 x 3153   linear   1005
+up15   1 x 1080 x 1920 x 3, uint8       1620 x 2880   both     1006
 =====  ===============================  ============  =======  ==========
 
 The "4k" frame (the 4K video frame of the pages' timing table, downscaled to
 1080p) is smooth per-channel gradients plus uniform noise; the others are
-uniform random bytes or uniform floats in [0, 1).
+uniform random bytes or uniform floats in [0, 1).  "up15" (a 1.5x
+enlargement of a camera frame) is not one of the pages' timed
+configurations; it measures the general enlargement path.
 """
 from __future__ import annotations
 
@@ -78,6 +81,7 @@ WORKLOADS = {
         Workload("up2x", 1, 1080, 1920, 1, "u8", 2160, 3840, ("linear", "nearest"), 1003, "uniform"),
         Workload("thumb", 256, 480, 640, 3, "u8", 224, 224, ("linear",), 1004, "uniform"),
         Workload("rgbaf", 1, 4320, 7680, 4, "f32", 5927, 3153, ("linear",), 1005, "uniform"),
+        Workload("up15", 1, 1080, 1920, 3, "u8", 1620, 2880, ("linear", "nearest"), 1006, "uniform"),
     )
 }
 
