@@ -646,15 +646,19 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
     return false;
 }
 
-// One-channel float32 linear row enlargements on tile_f32: the geometry,
-// budget and tile-height rule of the uint8 tiles, 8 pixels per lane (tiles
-// of 512 columns).  Grey 1080p -> 1620x2880: 13.55 -> 9.51 us against the
-// row-segment kernel.
+// One- and four-channel float32 linear row enlargements on tile_f32: the
+// geometry, budget and tile-height rule of the uint8 tiles, 8 pixels per
+// lane for one channel (tiles of 512 columns) and 1 for RGBA (64 columns,
+// so a lane's 16-byte result is one contiguous store).  Against the
+// row-segment / direct kernels: grey 1080p -> 1620x2880 13.55 -> 9.51 us,
+// RGBA 20.94 -> 19.69, the 4320x7680 -> 5927x3153 RGBA image 152.2 ->
+// 150.6 (its tiles stage 1.13 x the source, where the row-segment bands
+// fetched 1.23 x).  Float RGB stays on the direct kernel.
 template <int C, int TH>
 bool launch_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                      hipStream_t st, int &rc)
 {
-    constexpr int PX = C == 1 ? 8 : (C == 3 ? 4 : 2);
+    constexpr int PX = C == 1 ? 8 : (C == 3 ? 4 : 1);
     constexpr int COLS = 64 * PX;
     constexpr int PB = 4 * C;
     long long span = (long long)(COLS - 1) * W / dW + 3;
@@ -692,7 +696,7 @@ template <int C>
 bool try_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
                   hipStream_t st, int &rc, bool forced)
 {
-    constexpr int COLS = 64 * (C == 1 ? 8 : (C == 3 ? 4 : 2));
+    constexpr int COLS = 64 * (C == 1 ? 8 : (C == 3 ? 4 : 1));
     const long long per_image = (dW + COLS - 1) / COLS;
     const long long b16 = (long long)batch * ((dH + 15) / 16) * per_image;
     const long long b8 = (long long)batch * ((dH + 7) / 8) * per_image;
@@ -721,7 +725,7 @@ int linear_dispatch(const void *src, void *dst, int batch, int H, int W, int dH,
         if constexpr (sizeof(T) == 1) {
             if (try_tile_u8<C>(src, dst, batch, H, W, dH, dW, st, rc, path == Path::Tile))
                 return rc;
-        } else if constexpr (C == 1) {
+        } else if constexpr (C == 1 || C == 4) {
             if (try_tile_f32<C>(src, dst, batch, H, W, dH, dW, st, rc, path == Path::Tile))
                 return rc;
         }

@@ -2433,11 +2433,11 @@ __global__ __launch_bounds__(64 * kTileWaves) void tile_u8(
 // kernels' bit for bit.  The column table holds two words per column: the
 // byte offset of tap a from column sa << 1 | whether tap b is the next
 // column, and the weight's bits.  Source rows are 4-byte aligned, and so
-// is every staged pixel.  Launched for one channel: float RGB and RGBA
-// enlargements measured faster on the direct kernel, which gathers their
-// 12- and 16-byte pixels from cache and stages its stores (1080p ->
-// 1620x2880 RGBA 20.7 against 21.9 us here with staged stores, 31.6
-// without; 720p -> 1080p RGB 9.1 against 10.1 / 17.8).
+// is every staged pixel.  Launched for one channel (PX 8) and RGBA (PX 1,
+// one contiguous 16-byte store per lane).  Float RGB enlargements measured
+// faster on the direct kernel, which gathers their 12-byte pixels from
+// cache and stages its stores (720p -> 1080p RGB 9.1 against 10.1 us here
+// with the row staged for contiguous stores, 17.8 without).
 template <int C, int PX, int TH, int KL>
 __global__ __launch_bounds__(64 * kTileWaves) void tile_f32(
     const float *__restrict__ src, float *__restrict__ dst, int H, int W, int dH, int dW,

@@ -398,8 +398,9 @@ def test_tile_enlargements(shape, monkeypatch):
                   "tile %s" % (shape,))
 
 
-# one-channel float32 row enlargements: the float tiles (8 and 16 rows)
-@pytest.mark.parametrize("shape", [(2, 300, 500, 1, 800, 1300), (4, 300, 600, 1, 900, 1601)])
+# one-channel and RGBA float32 row enlargements: the float tiles (8 and 16 rows)
+@pytest.mark.parametrize("shape", [(2, 300, 500, 1, 800, 1300), (4, 300, 600, 1, 900, 1601),
+                                   (1, 300, 400, 4, 700, 901), (2, 400, 400, 4, 900, 900)])
 def test_tile_enlargements_f32(shape, monkeypatch):
     monkeypatch.delenv("MI_RESIZE_PATH", raising=False)
     N, H, W, C, dH, dW = shape
