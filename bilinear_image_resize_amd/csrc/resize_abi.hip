@@ -567,7 +567,7 @@ constexpr long long kTileLdsBudget = 64 * 1024;
 
 template <int C, int TH, bool NEAREST, int OUT>
 bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                    hipStream_t st, int &rc, int nn_map)
+                    hipStream_t st, int &rc, int nn_map, long long lds_cap = kTileLdsBudget)
 {
     constexpr int PX = C == 1 ? 8 : 4;
     constexpr int COLS = 64 * PX;
@@ -578,7 +578,7 @@ bool launch_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH,
     const long long pitch = 16 * (n16cap + 1);
     const long long rows_cap = (long long)(TH - 1) * H / dH + 3;
     const long long lds = (long long)COLS * 4 + rows_cap * pitch + 16;
-    if (lds > kTileLdsBudget) return false;
+    if (lds > lds_cap) return false;
     const long long chunks = (rows_cap * n16cap + 255) / 256;   // per thread, at most
     const int tiles_x = (dW + COLS - 1) / COLS, tiles_y = (dH + TH - 1) / TH;
     const long long blocks = (long long)batch * tiles_y * tiles_x;
@@ -627,6 +627,12 @@ constexpr long long kTileBlocks16 = 700;
 constexpr long long kTileBlocks8 = 512;
 constexpr long long kTileBlocks16One = 400;   // one channel
 constexpr long long kTileBlocks8One = 200;
+// and 16-row tiles only while one fits 24 KiB of LDS (six workgroups per
+// CU): the float RGBA image 4320x7680 -> 5927x3153, whose 2.4x column
+// downscale makes 16-row tiles 33 KiB, runs 150.2 us on them and 147.3 on
+// 8-row tiles (1080p -> 1620x2880 RGBA, 10 KiB tiles: 19.7 on 16 rows,
+// 22.6 on 8); the uint8 enlargements' 16-row tiles stay within ~20 KiB
+constexpr long long kTileLds16 = 24 * 1024;
 
 template <int C, bool NEAREST = false, int OUT = kOutSame>
 bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
@@ -638,8 +644,8 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
     const long long b8 = (long long)batch * ((dH + 7) / 8) * per_image;
     const long long min16 = C == 1 ? kTileBlocks16One : kTileBlocks16;
     const long long min8 = C == 1 ? kTileBlocks8One : kTileBlocks8;
-    if (b16 >= min16 &&
-        launch_tile_u8<C, 16, NEAREST, OUT>(src, dst, batch, H, W, dH, dW, st, rc, nn_map))
+    if (b16 >= min16 && launch_tile_u8<C, 16, NEAREST, OUT>(src, dst, batch, H, W, dH, dW, st, rc,
+                                                             nn_map, kTileLds16))
         return true;
     if (b8 >= min8 || forced)
         return launch_tile_u8<C, 8, NEAREST, OUT>(src, dst, batch, H, W, dH, dW, st, rc, nn_map);
@@ -656,7 +662,7 @@ bool try_tile_u8(const void *src, void *dst, int batch, int H, int W, int dH, in
 // fetched 1.23 x).  Float RGB stays on the direct kernel.
 template <int C, int TH>
 bool launch_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH, int dW,
-                     hipStream_t st, int &rc)
+                     hipStream_t st, int &rc, long long lds_cap = kTileLdsBudget)
 {
     constexpr int PX = C == 1 ? 8 : (C == 3 ? 4 : 1);
     constexpr int COLS = 64 * PX;
@@ -667,7 +673,7 @@ bool launch_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH
     const long long pitch = 16 * (n16cap + 1);
     const long long rows_cap = (long long)(TH - 1) * H / dH + 3;
     const long long lds = (long long)COLS * 8 + rows_cap * pitch + 16;
-    if (lds > kTileLdsBudget) return false;
+    if (lds > lds_cap) return false;
     const long long chunks = (rows_cap * n16cap + 255) / 256;
     const int tiles_x = (dW + COLS - 1) / COLS, tiles_y = (dH + TH - 1) / TH;
     const long long blocks = (long long)batch * tiles_y * tiles_x;
@@ -700,7 +706,8 @@ bool try_tile_f32(const void *src, void *dst, int batch, int H, int W, int dH, i
     const long long per_image = (dW + COLS - 1) / COLS;
     const long long b16 = (long long)batch * ((dH + 15) / 16) * per_image;
     const long long b8 = (long long)batch * ((dH + 7) / 8) * per_image;
-    if (b16 >= kTileBlocks16 && launch_tile_f32<C, 16>(src, dst, batch, H, W, dH, dW, st, rc))
+    if (b16 >= kTileBlocks16 &&
+        launch_tile_f32<C, 16>(src, dst, batch, H, W, dH, dW, st, rc, kTileLds16))
         return true;
     if (b8 >= kTileBlocks8 || forced)
         return launch_tile_f32<C, 8>(src, dst, batch, H, W, dH, dW, st, rc);
