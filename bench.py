@@ -55,30 +55,30 @@ INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 # traffic when they no longer hash to that value (the kernel changed since).
 MEASURED_TRAFFIC = {
     ("4k", "linear"): {"kernel": "linear_half_u8<3, false, false>",
-                       "profile": "profiles/pmc_traffic_all_workloads.md",
-                       "kernel_source_sha256_16": "e57aee3c6cce6bd2",
-                       "fetch_kib": 12175.019, "write_kib": 6075.0,
-                       "fetch_scale": 1.9985, "write_scale": 0.99882},
+                      "profile": "profiles/pmc_traffic_all_workloads.md",
+                      "kernel_source_sha256_16": "1e7d296ddc1f454c",
+                      "fetch_kib": 12171.034, "write_kib": 6075.0,
+                      "fetch_scale": 1.99832, "write_scale": 0.99912},
     ("up2x", "linear"): {"kernel": "linear_up2_u8<1, 4, true>",
-                         "profile": "profiles/pmc_traffic_all_workloads.md",
-                         "kernel_source_sha256_16": "e57aee3c6cce6bd2",
-                         "fetch_kib": 1033.62, "write_kib": 8100.0,
-                         "fetch_scale": 1.9985, "write_scale": 0.99882},
+                        "profile": "profiles/pmc_traffic_all_workloads.md",
+                        "kernel_source_sha256_16": "1e7d296ddc1f454c",
+                        "fetch_kib": 1040.6, "write_kib": 8100.0,
+                        "fetch_scale": 1.99832, "write_scale": 0.99912},
     ("thumb", "linear"): {"kernel": "rowseg<unsigned char, 3, false, 2, true, 0, false, 0, 0>",
-                          "profile": "profiles/pmc_traffic_all_workloads.md",
-                          "kernel_source_sha256_16": "e57aee3c6cce6bd2",
-                          "fetch_kib": 107568.509, "write_kib": 38596.418,
-                          "fetch_scale": 1.9985, "write_scale": 0.99882},
-    ("rgbaf", "linear"): {"kernel": "rowseg<float, 4, false, 4, false, 0, false, 0, 0>",
-                          "profile": "profiles/pmc_traffic_all_workloads.md",
-                          "kernel_source_sha256_16": "e57aee3c6cce6bd2",
-                          "fetch_kib": 322067.215, "write_kib": 296627.108,
-                          "fetch_scale": 1.99856, "write_scale": 0.99882},
-    ("up15", "linear"): {"kernel": "tile_u8<3, 4, 16, 2, false, 0>",
                          "profile": "profiles/pmc_traffic_all_workloads.md",
-                         "kernel_source_sha256_16": "e57aee3c6cce6bd2",
-                         "fetch_kib": 5430.615, "write_kib": 13668.751,
-                         "fetch_scale": 1.99856, "write_scale": 0.99882},
+                         "kernel_source_sha256_16": "1e7d296ddc1f454c",
+                         "fetch_kib": 107575.511, "write_kib": 38592.036,
+                         "fetch_scale": 1.99832, "write_scale": 0.99912},
+    ("rgbaf", "linear"): {"kernel": "tile_f32<4, 1, 8, 8>",
+                         "profile": "profiles/pmc_traffic_all_workloads.md",
+                         "kernel_source_sha256_16": "1e7d296ddc1f454c",
+                         "fetch_kib": 337077.912, "write_kib": 296628.469,
+                         "fetch_scale": 1.99856, "write_scale": 0.99912},
+    ("up15", "linear"): {"kernel": "tile_u8<3, 4, 16, 2, false, 0>",
+                        "profile": "profiles/pmc_traffic_all_workloads.md",
+                        "kernel_source_sha256_16": "1e7d296ddc1f454c",
+                        "fetch_kib": 5427.929, "write_kib": 13668.751,
+                        "fetch_scale": 1.99856, "write_scale": 0.99912},
 }
 
 
