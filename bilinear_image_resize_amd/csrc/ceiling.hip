@@ -6,8 +6,9 @@
 // kernel over a range of frame heights - plus a few kernels of its own that bound what any kernel of the
 // same shape can reach (an empty grid, a read-only stream, a stand-in
 // with the exact 2:1 kernel's loads, stores and grid that records when each
-// workgroup starts and ends, and stand-ins with the exact 2x kernel's grid
-// and byte mix).  It prints one JSON object per line.
+// workgroup starts and ends, stand-ins with the exact 2x kernel's grid
+// and byte mix, and one with the float RGBA enlargement's byte mix).  It
+// prints one JSON object per line.
 //
 // Timing follows the method of "From Prototype to Performance: Optimizing
 // OpenCV Resize on Volcanic GPUs" (section "Measure performance carefully":
@@ -220,6 +221,32 @@ double time_us(F launch, int iters, int S, hipStream_t *st)
 // Pseudo-random bytes (an integer hash of the index): kernels that do much
 // arithmetic per byte run measurably slower on random than on constant data
 // (the thumbnail batch 47.8 vs 44.4 us), so no buffer here is left constant.
+// Stand-in with the float RGBA enlargement's byte mix (4320 x 7680 -> 5927 x
+// 3153, 16-byte pixels): workgroup w reads source units [256 L w, 256 L (w +
+// 1)), L lane-strided 16-byte loads per lane, all in flight together, and
+// writes output units [o(w), o(w + 1)), o(w) = w nd16 / groups, lane
+// strided, with non-temporal stores of values that depend on every load of
+// the lane.  Every source byte is read once and every output byte written
+// once, in coalesced runs; ns16 is a multiple of 256 L (the caller checks).
+template <int L>
+__global__ __launch_bounds__(256) void mix_standin(const u32x4 *__restrict__ s, u32x4 *__restrict__ d,
+                                                   long long nd16)
+{
+    const long long s0 = (long long)blockIdx.x * (256 * L);
+    u32x4 acc = {0, 0, 0, 0};
+    u32x4 v[L];
+#pragma unroll
+    for (int r = 0; r < L; ++r) v[r] = s[s0 + threadIdx.x + 256 * r];
+#pragma unroll
+    for (int r = 0; r < L; ++r) acc ^= v[r];
+    const long long o0 = (long long)blockIdx.x * nd16 / gridDim.x;
+    const long long o1 = ((long long)blockIdx.x + 1) * nd16 / gridDim.x;
+    for (long long o = o0 + threadIdx.x; o < o1; o += 256) {
+        acc.x += 1u;
+        __builtin_nontemporal_store(acc, d + o);
+    }
+}
+
 __global__ void fill_hash(uint32_t *p, size_t n, uint32_t seed)
 {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
@@ -416,6 +443,51 @@ void up2_byte_mix(hipStream_t *st)
     report("copy of the same bytes, half read and half written", time_us(cp, 400, 1, st), sb + db);
 }
 
+// The float RGBA resize 4320 x 7680 -> 5927 x 3153 (rows enlarge 1.372x,
+// columns shrink 2.436x) beside the stand-in with its byte mix (every
+// source byte read once, every output byte written once) and a copy of the
+// same bytes split evenly between reads and writes.  Two buffer pairs of
+// 830 MB rotate, so no launch finds its source in the Infinity Cache.
+void rgbaf_byte_mix(hipStream_t *st)
+{
+    constexpr int H = 4320, W = 7680, DH = 5927, DW = 3153;
+    const long long sb = 16ll * H * W, db = 16ll * DH * DW;
+    const int pairs = 2;
+    Ring srcs((size_t)sb, pairs), dsts((size_t)db, pairs);
+    auto report = [&](const char *what, double us, long long bytes) {
+        printf("{\"section\": \"rgbaf_byte_mix\", \"what\": \"%s\", \"bytes\": %lld, \"us\": %.3f, "
+               "\"GBps\": %.1f, \"frac_of_peak\": %.4f}\n",
+               what, bytes, us, bytes / (us * 1e3), bytes / (us * 1e3) / kPeakGBps);
+    };
+    const long long ns16 = sb / 16, nd16 = db / 16;
+    auto standin = [&](auto kernel, int loads, const char *what) {
+        if (ns16 % (256 * loads) != 0) exit(4);
+        const unsigned groups = (unsigned)(ns16 / (256 * loads));
+        auto mix = [&](int i, hipStream_t s) {
+            hipLaunchKernelGGL(kernel, dim3(groups), dim3(256), 0, s,
+                               (const u32x4 *)srcs.p[i % pairs], (u32x4 *)dsts.p[i % pairs], nd16);
+        };
+        report(what, time_us(mix, 40, 1, st), sb + db);
+    };
+    standin(mix_standin<4>, 4, "stand-in, source read once and output written once, 4 loads per lane");
+    standin(mix_standin<8>, 8, "stand-in, source read once and output written once, 8 loads per lane");
+    standin(mix_standin<16>, 16, "stand-in, source read once and output written once, 16 loads per lane");
+    auto rs = [&](int i, hipStream_t s) {
+        if (resize_linear(srcs.p[i % pairs], dsts.p[i % pairs], 1, H, W, 4, MI_RESIZE_F32, DH, DW,
+                          s) != 0)
+            exit(3);
+    };
+    report("resize_linear float RGBA", time_us(rs, 40, 1, st), sb + db);
+    // the same-bytes copy: (sb + db) / 2 each way, from the sources (each
+    // larger than that) into a ring of its own
+    const long long half = (sb + db) / 2;
+    Ring other((size_t)half, pairs);
+    auto cp = [&](int i, hipStream_t s) {
+        if (resize_copy_bytes(srcs.p[i % pairs], other.p[(i + 1) % pairs], half, s) != 0) exit(2);
+    };
+    report("copy of the same bytes, half read and half written", time_us(cp, 40, 1, st), sb + db);
+}
+
 void trace_4k(hipStream_t *st)
 {
     const long long sb = 24883200, db = 6220800;
@@ -480,7 +552,7 @@ int main(int argc, char **argv)
         {"copy_vs_size", copy_vs_size},   {"empty_grid", empty_grids},
         {"read_only", read_only_stream},  {"resize_4k_rgb", resize_4k},
         {"resize_rgb_2to1_rows", resize_rows_fit}, {"trace_4k_rgb_standin", trace_4k},
-        {"up2x_byte_mix", up2_byte_mix}};
+        {"up2x_byte_mix", up2_byte_mix}, {"rgbaf_byte_mix", rgbaf_byte_mix}};
     for (const auto &sec : sections) {
         if (!want(sec.name)) continue;
         sec.run(st);
