@@ -124,6 +124,43 @@ def test_random_shapes(dtype, mode, path, monkeypatch):
                       "random #%d %s" % (i, (N, H, W, C, dH, dW)))
 
 
+@pytest.mark.parametrize("path", ["auto"] + PATHS)
+@pytest.mark.parametrize("op", ["grey", "roi", "mirror", "wrap"])
+def test_random_shapes_other_entry_points(op, path, monkeypatch):
+    """The fused grey output, per-image regions (some partly or wholly
+    outside the image, clamped by both sides) and the mirror / wrap borders
+    on random shapes, uint8 and float32, on every kernel family."""
+    if path != "auto":
+        monkeypatch.setenv("MI_RESIZE_PATH", path)
+    r = np.random.default_rng(4242 + 8 * ["grey", "roi", "mirror", "wrap"].index(op) +
+                              (["auto"] + PATHS).index(path))
+    for i in range(30):
+        N, H, W, C, dH, dW = random_case(r)
+        if op == "grey" and C == 1:
+            C = 3
+        dtype = "u8" if r.random() < 0.7 else "f32"
+        s = random_image(r, (N, H, W, C), dtype)
+        src = torch.from_numpy(s).cuda()
+        dC = 1 if op == "grey" else C
+        dst = torch.empty((N, dH, dW, dC), dtype=src.dtype, device="cuda")
+        say("case random %s %s %s #%d N=%d H=%d W=%d C=%d -> %dx%d" % (op, dtype, path, i, N, H, W, C, dH, dW))
+        if op == "grey":
+            R.resize_linear_grey(src, dst)
+            want = oracle.resize_linear_grey(s, dH, dW)
+        elif op == "roi":
+            rois = np.array([(int(r.integers(-3, W)), int(r.integers(-3, H)),
+                              int(r.integers(0, W + 4)), int(r.integers(0, H + 4)))
+                             for _ in range(N)], dtype=np.int32)
+            R.resize_linear_roi(src, dst, torch.from_numpy(rois).cuda())
+            want = oracle.resize_linear_roi(s, rois, dH, dW)
+        else:
+            R.resize_linear_border(src, dst, border=op)
+            want = oracle.resize_linear(s, dH, dW, border=op)
+        torch.cuda.synchronize()
+        assert_parity(dst.cpu().numpy().reshape(want.shape), want,
+                      "random %s #%d %s" % (op, i, (N, H, W, C, dH, dW, dtype)))
+
+
 # --------------------------------------------------------------------------
 # exact 2:1 downscale (its own kernel) for every channel count, ragged batch,
 # and the shapes just off its conditions (which take the generic kernel)
